@@ -1,0 +1,78 @@
+"""Paged decode attention, fp64 (oracle; test infrastructure only).
+
+Definition followed:
+* Address translation ("pagedattention vllm" glossary, chipfoundryservices,
+  "Attention Computation > Address Translation"; "PagedAttention",
+  lastdictionary): logical token t of sequence s lives in physical block
+  block_tables[s, t // B] at in-block offset t % B.  Cache layout
+  [num_blocks, num_kv_heads, B, head_dim] for both keys and values.
+* Block-wise attention (same glossary, "Attention Computation > Block-Wise
+  Attention"; systemdesign.academy glossary "Paged Attention"): the blocks are
+  gathered and attention is computed as if they were contiguous, which is
+  mathematically standard attention.  So the oracle gathers each sequence
+  into contiguous fp64 arrays and evaluates
+
+      x_t = scale * <q, K_t>,   p = softmax(x),   out = sum_t p_t V_t
+
+  over the L = context_lens[s] tokens of the sequence, all in fp64.
+* Query head j reads key/value head j // (num_q_heads / num_kv_heads) (heads
+  sharing one set of keys and values, systemdesign.academy glossary; the
+  grouping into contiguous runs of query heads is a reading, not on the pages).
+* The scale is taken as the fp32 value the library receives, widened to fp64.
+* A sequence of length 0 has an all-zero output row (the pages are silent).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import decode
+
+
+def gather_sequence(cache, table_row, length: int, kv_head: int, block_size: int) -> np.ndarray:
+    """Contiguous [length, head_dim] view of one sequence's cached rows for one KV head.
+
+    `cache` is an array (or anything that supports cache[int_array, int]
+    indexing and returns a numpy array) laid out [num_blocks, Hkv, B, D]."""
+    n_blocks = -(-int(length) // block_size)
+    phys = np.asarray(table_row[:n_blocks], dtype=np.int64)
+    num_blocks = cache.shape[0]
+    if phys.size and (phys.min() < 0 or phys.max() >= num_blocks):
+        raise ValueError("block table entry outside the pool")
+    tiles = np.asarray(cache[phys, kv_head])            # [n_blocks, B, D]
+    return tiles.reshape(n_blocks * block_size, tiles.shape[-1])[:length]
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           block_size: int, num_kv_heads: int, dtype: str, rows=None) -> np.ndarray:
+    """fp64 decode attention through the block tables.
+
+    q: [S, Hq, D] in storage format; caches [N, Hkv, B, D]; block_tables int
+    [S, M]; context_lens int [S].  Returns fp64 [S, Hq, D], or, when `rows`
+    lists (s, j) pairs, an fp64 [len(rows), D] array in that order."""
+    S, Hq, D = q.shape
+    if Hq % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = Hq // num_kv_heads
+    scale64 = float(np.float32(scale))
+    wanted = [(s, j) for s in range(S) for j in range(Hq)] if rows is None else [tuple(map(int, r)) for r in rows]
+
+    by_kv = {}
+    for idx, (s, j) in enumerate(wanted):
+        by_kv.setdefault((s, j // group), []).append((idx, j))
+
+    result = np.zeros((len(wanted), D), dtype=np.float64)
+    for (s, h), members in by_kv.items():
+        L = int(context_lens[s])
+        if L <= 0:
+            continue
+        K = decode(gather_sequence(k_cache, block_tables[s], L, h, block_size), dtype)
+        V = decode(gather_sequence(v_cache, block_tables[s], L, h, block_size), dtype)
+        for idx, j in members:
+            qv = decode(q[s, j], dtype)
+            x = scale64 * (K @ qv)
+            e = np.exp(x - x.max())
+            p = e / e.sum()
+            result[idx] = p @ V
+    if rows is None:
+        return result.reshape(S, Hq, D)
+    return result

@@ -1,0 +1,51 @@
+"""Cache scatter and block copy, bitwise (oracle; test infrastructure only).
+
+* reshape_and_cache: the new token's key and value are stored into the cache
+  block the block table names ("What is PagedAttention" (tecyfy), "How it
+  works"): token i goes to block slot_mapping[i] // B at offset
+  slot_mapping[i] % B, all KV heads; a negative slot means "do not store".
+* copy_blocks: the copy made before a shared block is modified
+  ("pagedattention vllm" glossary, "Copy-on-Write Sharing > Divergence
+  Handling"): for each (src, dst) pair, block dst of both caches becomes a
+  copy of block src, all heads and offsets.
+
+Both move bit patterns only.  Pairs must have distinct destinations and no
+destination may also be a source in the same call; then the result does not
+depend on the order pairs are applied in.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _bits(a: np.ndarray) -> np.ndarray:
+    return a.view({1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size: int) -> None:
+    """In place.  k, v: [T, Hkv, D]; caches [N, Hkv, B, D]; slot_mapping [T]."""
+    kc, vc, kb, vb = _bits(k_cache), _bits(v_cache), _bits(k), _bits(v)
+    num_blocks = kc.shape[0]
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, block_size)
+        if block >= num_blocks:
+            raise ValueError(f"slot {slot} outside the pool")
+        kc[block, :, offset, :] = kb[i]
+        vc[block, :, offset, :] = vb[i]
+
+
+def copy_blocks(k_cache, v_cache, pairs) -> None:
+    """In place.  pairs: iterable of (src, dst) physical block ids."""
+    pairs = [tuple(map(int, p)) for p in np.asarray(pairs).reshape(-1, 2)]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts) or set(dsts) & {s for s, _ in pairs}:
+        raise ValueError("copy pairs need distinct destinations that are not sources")
+    kc, vc = _bits(k_cache), _bits(v_cache)
+    num_blocks = kc.shape[0]
+    for src, dst in pairs:
+        if not (0 <= src < num_blocks and 0 <= dst < num_blocks):
+            raise ValueError("block id outside the pool")
+        kc[dst] = kc[src]
+        vc[dst] = vc[src]

@@ -1,0 +1,82 @@
+"""Decode workloads for paged attention, as plain data.
+
+Each workload is one decode step over a batch of sequences whose keys and
+values sit in fixed-size blocks of a shared physical pool.  The shapes are
+those of single attention layers of well-known models (no weights are
+involved); every value is drawn from N(0, 1).
+
+Nothing in this package computes attention, scatters a token or copies a
+block: it only decides lengths, block placement and input values, so that the
+CPU oracle and the GPU library can be fed identical bits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+import math
+
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str              # "f32" | "f16" | "bf16"
+    block_size: int
+    lengths: str            # "fixed" | "uniform" | "lognormal" | "shared_prefix"
+    fixed_lengths: tuple = ()
+    len_lo: int = 1
+    len_hi: int = 1
+    lognormal_median: float = 0.0
+    lognormal_sigma: float = 1.0
+    pool_blocks: int = 0    # explicit pool size; 0 = ceil(pool_factor * need)
+    pool_factor: float = 1.2
+    partition_size: int = 0  # split-K partition in tokens; 0 = library default
+    prompt_len: int = 0      # shared-prefix workloads only
+    samples_per_prompt: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def dtype_bytes(self) -> int:
+        return DTYPE_BYTES[self.dtype]
+
+    def scaled(self, **kw) -> "DecodeConfig":
+        return replace(self, **kw)
+
+
+# The five decode workloads.  Shapes: Llama-2-7B (32 heads), Llama-2-13B
+# (40 heads) and a 70B-class grouped-query layer (64 query heads over 8 KV
+# heads); block size 16 is the default the glossary pages give, 32 the size
+# one of them recommends for balance.
+CONFIGS = {
+    1: DecodeConfig("tiny_mha_f32", num_seqs=4, num_q_heads=2, num_kv_heads=2,
+                    head_dim=64, dtype="f32", block_size=16, lengths="fixed",
+                    fixed_lengths=(5, 17, 33, 64), pool_blocks=32),
+    2: DecodeConfig("llama2_7b_layer_f16", num_seqs=64, num_q_heads=32, num_kv_heads=32,
+                    head_dim=128, dtype="f16", block_size=16, lengths="uniform",
+                    len_lo=128, len_hi=2048),
+    3: DecodeConfig("llama2_13b_layer_bf16", num_seqs=128, num_q_heads=40, num_kv_heads=40,
+                    head_dim=128, dtype="bf16", block_size=16, lengths="lognormal",
+                    lognormal_median=400.0, lognormal_sigma=1.0, len_lo=1, len_hi=4096),
+    4: DecodeConfig("gqa70b_layer_bf16", num_seqs=256, num_q_heads=64, num_kv_heads=8,
+                    head_dim=128, dtype="bf16", block_size=32, lengths="uniform",
+                    len_lo=1024, len_hi=32768, partition_size=512),
+    5: DecodeConfig("shared_prefix_sampling_bf16", num_seqs=512, num_q_heads=40, num_kv_heads=40,
+                    head_dim=128, dtype="bf16", block_size=16, lengths="shared_prefix",
+                    len_lo=1, len_hi=512, prompt_len=1000, samples_per_prompt=8),
+}
+
+
+def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, dtype: str) -> int:
+    """Logical K+V bytes one decode step reads: sum(L) * Hkv * D * 2 * bytes."""
+    return int(sum(int(x) for x in context_lens)) * num_kv_heads * head_dim * 2 * DTYPE_BYTES[dtype]
