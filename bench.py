@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-attention decode step on one MI355X.
+
+A step is the whole decode hot path for one batch: reshape_and_cache of the
+token each sequence appends (plus copy_blocks when the workload has
+copy-on-write pairs), then paged decode attention over all cached tokens
+(main kernel + split-K reduce).  Inputs are synthetic, seeded, N(0, 1), and
+resident in HBM before timing starts.  The default workload is a
+Llama-2-7B-shaped layer: batch 64, 32 heads, head_dim 128, fp16 KV cache in
+16-token blocks, context lengths uniform in [128, 2048], blocks scattered at
+random over a pool 1.2x the need.
+
+Prints ONE JSON line:
+  value        KV GB/s read per step (sum(L) * Hkv * D * 2 * bytes / step time)
+  roofline     the main attention kernel: algorithmic bytes per launch / its
+               average duration (HIP events on its stream) vs 8 TB/s HBM
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
+               on this host's cores (a reported baseline, not the target)
+
+    python bench.py [--steps K] [--warmup W] [--config {1..5}] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synthetic import CONFIGS, DTYPE_BYTES, host_values, kv_bytes, make_layout  # noqa: E402
+
+METRIC = "paged decode attn: KV GB/s read (% of HBM peak) + seq·heads/sec, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+LENGTH_DESC = {
+    1: "fixed {5,17,33,64}",
+    2: "uniform [128, 2048]",
+    3: "lognormal median 400 sigma 1.0, clipped [1, 4096]",
+    4: "uniform [1024, 32768]",
+    5: "1000-token shared prompt + uniform [1, 512] per-sample tail",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, run before the GPU is touched (the worker pool
+# forks), over a bounded sample of sequences of the same workload.
+# ---------------------------------------------------------------------------
+_CPU = {}
+
+
+def _oracle_rows(s):
+    import oracle
+    c = _CPU
+    cfg = c["cfg"]
+    oracle.paged_attention_decode(c["q"][s:s + 1], c["k"], c["v"], c["tables"][s:s + 1], c["lens"][s:s + 1],
+                                  cfg.scale, cfg.block_size, cfg.num_kv_heads, cfg.dtype)
+    return s
+
+
+def cpu_baseline(cfg, layout, cpu_seconds: float):
+    import multiprocessing as mp
+
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16))
+    spp = cfg.samples_per_prompt or 1
+    # Enough sequences to keep every worker busy, but a pool small enough to
+    # draw on the host in seconds (about 2.5e8 cached values).
+    per_seq = layout.context_lens.astype(np.int64) * cfg.num_kv_heads * cfg.head_dim * 2
+    k, acc = 0, 0
+    while k < len(per_seq) and (k < workers or acc < 2.5e8):
+        acc += int(per_seq[k])
+        k += 1
+        if acc >= 2.5e8 and k >= spp:
+            break
+    k = min(len(per_seq), -(-k // spp) * spp)
+    workers = min(workers, k)
+    lens = layout.context_lens[:k]
+    sub = make_layout(cfg.scaled(num_seqs=k), seed=1000 + k, lengths=lens)
+    host = host_values(sub)
+    _CPU.update(cfg=cfg, q=host.q, k=host.k_cache, v=host.v_cache, tables=sub.block_tables,
+                lens=sub.context_lens)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_rows, range(k), chunksize=1)
+        one = time.perf_counter() - t0
+        reps = int(min(20, max(1, math.ceil(cpu_seconds / workers / max(one, 1e-3)))))
+        t0 = time.perf_counter()
+        pool.map(_oracle_rows, list(range(k)) * reps, chunksize=1)
+        elapsed = time.perf_counter() - t0
+    nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.dtype) * reps
+    return {
+        "value": round(nbytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"first {k} of {len(layout.context_lens)} sequences (all {cfg.num_q_heads} heads, "
+                   f"their real lengths, sum {int(lens.sum())} tokens) x {reps} passes, fp64 numpy, "
+                   f"{workers} worker processes, {elapsed:.2f} s wall"),
+        "seq_heads_per_s": round(k * reps * cfg.num_q_heads / elapsed, 2),
+    }
+
+
+# ---------------------------------------------------------------------------
+# HIP events on the launch stream (ctypes on the HIP runtime).
+# ---------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="split-K partition in tokens (0 = library default; -1 = the workload's own)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(the decode step shards by KV head or by sequence with no exchange); run with --gpus 1")
+        sys.exit(2)
+
+    cfg = CONFIGS[args.config]
+    seed = args.config if args.seed is None else args.seed
+    layout = make_layout(cfg, seed=seed)
+    part = cfg.partition_size if args.partition_size < 0 else args.partition_size
+    S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    es = DTYPE_BYTES[cfg.dtype]
+    step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.dtype)
+    log(f"workload {cfg.name}: S={S} Hq={Hq} Hkv={Hkv} D={D} B={B} {cfg.dtype} sum(L)={int(layout.context_lens.sum())} "
+        f"pool={layout.num_blocks} blocks KV/step={step_kv / 1e9:.3f} GB")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(cfg, layout, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} cores")
+
+    import torch
+    import paged_kv_cache_339_amd as pkv
+    from paged_kv_cache_339_amd._lib import KERNELS, AttnOptions, lib
+    from paged_kv_cache_339_amd.ops import dtype_code
+    from synthetic import device_values
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, kc, vc, kn, vn = device_values(layout, device=dev)
+
+    def ints(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    tables, lens, slots = ints(layout.block_tables), ints(layout.context_lens), ints(layout.new_slots)
+    # Copy-on-write pairs into spare blocks (destinations distinct from every source).
+    n_pairs = len(layout.cow_pairs)
+    pairs = None
+    if n_pairs:
+        spare = layout.pool_order[layout.used_blocks:layout.used_blocks + n_pairs]
+        assert len(spare) == n_pairs, "pool has no room for the copy-on-write destinations"
+        pairs = ints(np.stack([layout.cow_pairs[:, 0], spare], axis=1))
+    out = torch.empty_like(q)
+    code = dtype_code(q)
+    max_ctx = layout.max_context_len
+    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    vp = ctypes.c_void_p
+    scatter_args = (vp(kn.data_ptr()), vp(vn.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                    vp(slots.data_ptr()), S, Hkv, D, B, layout.num_blocks, code, vp(stream))
+    copy_args = None
+    if pairs is not None:
+        copy_args = (vp(kc.data_ptr()), vp(vc.data_ptr()), vp(pairs.data_ptr()), n_pairs, Hkv, B, D,
+                     layout.num_blocks, code, vp(stream))
+
+    def attn_args(opts):
+        return (vp(out.data_ptr()), vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                vp(tables.data_ptr()), vp(lens.data_ptr()), cfg.scale, B, Hkv, S, Hq, D,
+                layout.block_tables.shape[1], max_ctx, layout.num_blocks, code, vp(ws.data_ptr()),
+                ws.numel(), ctypes.byref(opts), vp(stream))
+
+    K, W = args.steps, args.warmup
+    begins = [ev.create() for _ in range(K)]
+    ends = [ev.create() for _ in range(K)]
+    plain = AttnOptions(part, KERNELS[args.kernel], None, None)
+    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i]) for i in range(K)]
+    warm_args = attn_args(plain)
+    timed_args = [attn_args(o) for o in timed]
+
+    def step(a):
+        if copy_args is not None:
+            st = lib.pkv_copy_blocks(*copy_args)
+            assert st == 0, st
+        st = lib.pkv_reshape_and_cache(*scatter_args)
+        assert st == 0, st
+        st = lib.pkv_paged_attention_decode(*a)
+        assert st == 0, st
+
+    for _ in range(W):
+        step(warm_args)
+    torch.cuda.synchronize()
+
+    t_start, t_stop = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.record(t_start, stream)
+    for i in range(K):
+        step(timed_args[i])
+    ev.record(t_stop, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.ms(t_start, t_stop)
+    main_ms = [ev.ms(begins[i], ends[i]) for i in range(K)]
+    ev.close()
+    assert torch.isfinite(out.float()).all().item(), "non-finite attention output"
+
+    step_s = total_ms / 1e3 / K
+    main_s = float(np.mean(main_ms)) / 1e3
+    nblk = -(-layout.context_lens // B)
+    alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4
+    achieved = alg_bytes / main_s / 1e9
+    kv_gbps = step_kv / step_s / 1e9
+    kernel_used = args.kernel if args.kernel != "auto" else (
+        "mfma" if (cfg.dtype != "f32" and Hq // Hkv in (4, 8, 16)) else "valu")
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "batch": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B,
+            "kv_dtype": cfg.dtype, "context_lens": LENGTH_DESC[args.config],
+            "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
+            "kv_bytes_per_step": step_kv, "partition_size": part, "kernel": kernel_used,
+            "step": ("copy_blocks + " if copy_args else "") + "reshape_and_cache + paged_attention_decode",
+        },
+        "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
+        "seq_heads_per_s": round(S * Hq / step_s, 1),
+        "attention_main_us": round(main_s * 1e6, 2),
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": f"attn_{kernel_used}_kernel",
+            "bytes_per_launch": int(alg_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

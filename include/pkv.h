@@ -1,0 +1,241 @@
+/*
+ * pkv.h — paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Plain pointers and sizes only.  "Device pointer" means
+ * memory the HIP runtime allocated on the GPU the call runs on; "stream" is a
+ * hipStream_t passed as void* (NULL = the default stream of the current
+ * device).  Device calls are asynchronous and ordered on `stream`; none of
+ * them synchronises, allocates or frees memory.  The caller owns every
+ * buffer.  Every entry point returns PKV_OK (0) or a negative status; host
+ * argument checks run before anything is launched, so a failed check leaves
+ * all memory untouched.  No C++ exception crosses this boundary.
+ *
+ * What the operations are (pages on PagedAttention):
+ *  - "PagedAttention" (lastdictionary): the KV cache of a sequence lives in
+ *    fixed-size blocks of e.g. 16 tokens scattered anywhere in GPU memory; a
+ *    per-sequence block table maps token positions to physical blocks; the
+ *    attention kernel reads keys and values through that table; blocks are
+ *    shared copy-on-write among sequences with a common prefix.
+ *  - "pagedattention vllm" glossary (chipfoundryservices), "Attention
+ *    Computation": block-wise attention equals standard attention over the
+ *    gathered blocks; address translation maps virtual to physical blocks,
+ *    loads them, computes and stores the result.  "Copy-on-Write Sharing":
+ *    reference counts; copy a shared block before a sequence modifies it.
+ *    "Memory Management": a free list, allocate on demand, release when the
+ *    sequence completes.  "Implementation Details": block table entries are
+ *    4 bytes.
+ *
+ * Layouts (all row-major, densely packed):
+ *   q, out            [num_seqs, num_q_heads, head_dim]
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq]; entry t of row s
+ *                     is the physical block holding tokens [t*B, (t+1)*B)
+ *   context_lens      int32 [num_seqs]; tokens attended by each sequence
+ *   k, v (new tokens) [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping      int32 [num_tokens]; slot = block * block_size + offset
+ *   src_dst_pairs     int32 [num_pairs, 2]; (source block, destination block)
+ * Query head j reads KV head j / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* a size is negative, zero where it may not be, or inconsistent */
+  PKV_ERR_DTYPE = -3,       /* unknown dtype */
+  PKV_ERR_UNSUPPORTED = -4, /* a valid combination this build has no kernel for */
+  PKV_ERR_ALIGN = -5,       /* a data pointer is not 16-byte aligned */
+  PKV_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small */
+  PKV_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch */
+  PKV_ERR_NO_BLOCKS = -8,   /* block manager: the free list is empty */
+  PKV_ERR_STATE = -9,       /* block manager: unknown/duplicate sequence, bad block */
+  PKV_ERR_CAPACITY = -10    /* an output buffer is too small */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_str(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention                                                          */
+/* ------------------------------------------------------------------------ */
+
+enum pkv_kernel {
+  PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit data with 4..16 query heads per KV head, else VALU */
+  PKV_KERNEL_VALU = 1,  /* vector-ALU kernel: 1, 2, 4 or 8 query heads per KV head */
+  PKV_KERNEL_MFMA = 2   /* matrix-core kernel: f16/bf16, 4, 8 or 16 query heads per KV head */
+};
+
+typedef struct pkv_attn_options {
+  /* Tokens per split-K partition.  0 = automatic; otherwise a positive
+   * multiple of block_size (and of 32 for the MFMA kernel).  A sequence of
+   * length L is cut into ceil(L / partition_size) partitions that are
+   * processed by separate workgroups and merged by a reduce kernel. */
+  int32_t partition_size;
+  int32_t kernel;            /* enum pkv_kernel */
+  /* Optional hipEvent_t handles (NULL = none), recorded on the stream right
+   * before and right after the main attention kernel, so a caller can time
+   * that kernel alone.  The reduce kernel, if any, runs after main_end. */
+  void* main_begin_event;
+  void* main_end_event;
+} pkv_attn_options;
+
+/* Bytes of split-K workspace pkv_paged_attention_decode needs for these
+ * sizes and options (0 when no sequence can span two partitions).  Returns
+ * 0 on invalid arguments as well; the decode call reports those. */
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_context_len,
+                                           pkv_dtype dtype, const pkv_attn_options* opts);
+
+/*
+ * Single-token decode attention through the block tables
+ * ("pagedattention vllm" glossary, Attention Computation: Block-Wise
+ * Attention and Address Translation; "What is PagedAttention" (tecyfy),
+ * How it works: attention rewritten to read keys and values from scattered
+ * blocks).  For every sequence s and query head j, with h = j / (Hq / Hkv)
+ * and L = context_lens[s]:
+ *
+ *   K_t = k_cache[block_tables[s][t / B]][h][t % B][:],  V_t likewise, t < L
+ *   out[s][j][:] = sum_t softmax_t(scale * <q[s][j], K_t>) * V_t
+ *
+ * computed in fp32 and rounded to the data type (round to nearest even).
+ * L = 0 gives a zero row.  Only the first ceil(L/B) table entries of a row
+ * are read and only the first L tokens are used; other pool slots may hold
+ * anything (NaN included) without affecting the result.
+ *
+ * Device pointers: out, q, k_cache, v_cache (16-byte aligned), block_tables,
+ * context_lens, workspace.  max_context_len (host) must be >= every
+ * context_lens[s]; it sizes the launch.  num_blocks is the pool size.
+ * Data errors are contained, never dereferenced: a table entry outside
+ * [0, num_blocks), or context_lens[s] above max_context_len or
+ * max_blocks_per_seq * B, makes that sequence's output rows NaN.
+ * head_dim: 64 or 128.  block_size: 8, 16, 32 or 64.
+ * workspace: device memory of at least pkv_paged_attention_workspace_bytes
+ * (may be NULL when that is 0); its contents need no initialisation.
+ * opts may be NULL (automatic everything).
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int32_t block_size, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t num_blocks, pkv_dtype dtype,
+                               void* workspace, size_t workspace_bytes,
+                               const pkv_attn_options* opts, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Cache write and copy-on-write                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Store each new token's key and value into the block slot the block
+ * manager reserved for it ("What is PagedAttention" (tecyfy), How it works:
+ * blocks handed out as the sequence grows):
+ *   k_cache[slot / B][h][slot % B][:] = k[i][h][:]   (and v), all h,
+ * for every i with 0 <= slot = slot_mapping[i] < num_blocks * B.  Negative
+ * slots are skipped (padding); slots at or beyond the pool are skipped too
+ * (a data error, never written).  Bitwise copy.  Two tokens naming the same
+ * slot is a caller error (which one lands is unspecified).
+ * Device pointers: k, v, k_cache, v_cache (16-byte aligned), slot_mapping.
+ */
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          pkv_dtype dtype, void* stream);
+
+/*
+ * Copy-on-write block copies ("pagedattention vllm" glossary, Copy-on-Write
+ * Sharing: Divergence Handling): for every pair p, block dst = pairs[p][1]
+ * of both caches becomes a bitwise copy of block src = pairs[p][0], all KV
+ * heads and offsets.  Destinations must be distinct and must not be sources
+ * in the same call (the block manager guarantees it); then pair order does
+ * not matter.  Pairs naming a block outside [0, num_blocks) are skipped.
+ * Device pointers: k_cache, v_cache (16-byte aligned), src_dst_pairs.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, int32_t num_pairs,
+                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t num_blocks,
+                    pkv_dtype dtype, void* stream);
+
+/*
+ * Debug/test helper: materialise one KV head's keys of a set of sequences
+ * contiguously, through the block tables:
+ *   dst[s][t][:] = cache[block_tables[s][t / B]][kv_head][t % B][:],  t < context_lens[s],
+ * rows t >= context_lens[s] (up to max_context_len) are left untouched.
+ * dst: device [num_seqs, max_context_len, head_dim].  Out-of-pool table
+ * entries are skipped.  Same layout rules as the attention call.
+ */
+int pkv_gather_kv(void* dst, const void* cache, const int32_t* block_tables,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                  int32_t max_context_len, int32_t kv_head, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks, pkv_dtype dtype,
+                  void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block manager (free list, reference counts, block tables, CoW)       */
+/* ------------------------------------------------------------------------ */
+/*
+ * "What is PagedAttention" (tecyfy), How it works: blocks are handed out as a
+ * sequence grows; a sequence holds the blocks it filled plus part of the
+ * last.  "pagedattention vllm" glossary: Memory Management > Block
+ * Allocation (free list, allocate on demand, release on completion);
+ * Copy-on-Write Sharing > Reference Counting and Divergence Handling.
+ *
+ * Policy: blocks leave the free list from its front; blocks whose count
+ * drops to zero return to its front in table order.  Appending at position
+ * t allocates a new block when t % B == 0; otherwise, if the last block has
+ * more than one reference, it takes a fresh block for this sequence, reports
+ * (shared, fresh) for pkv_copy_blocks, and drops one reference of the
+ * shared block.  Host memory only, no GPU needed; a handle is not
+ * thread-safe.  Sequence ids are in [0, max_seqs).
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* free_order: NULL (0, 1, ..., num_blocks-1) or a permutation of the pool,
+ * front first.  Returns NULL on invalid arguments or out of memory. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                                 const int32_t* free_order);
+void pkv_bm_destroy(pkv_block_manager* bm);
+int pkv_bm_add_seq(pkv_block_manager* bm, int32_t seq);
+/* child gets parent's table and length; each shared block gains a reference */
+int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child);
+/* Reserve the next token's slot.  *cow_src / *cow_dst receive the pair to
+ * copy before the write, or -1 / -1.  PKV_ERR_NO_BLOCKS leaves all state
+ * unchanged. */
+int pkv_bm_append(pkv_block_manager* bm, int32_t seq, int32_t* slot, int32_t* cow_src,
+                  int32_t* cow_dst);
+/* One append for each of n sequences, in order.  slots[n]; copy pairs are
+ * written to pairs[2*k], pairs[2*k+1] and counted in *num_pairs (pairs_cap
+ * pairs of room).  On an error at sequence i the appends before i stay
+ * done, the return value is the error, and *num_done = i. */
+int pkv_bm_append_batch(pkv_block_manager* bm, const int32_t* seqs, int32_t n, int32_t* slots,
+                        int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs, int32_t* num_done);
+/* Release a finished sequence's blocks. */
+int pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq);
+/* Length of a sequence (>= 0) or a negative status. */
+int pkv_bm_seq_len(const pkv_block_manager* bm, int32_t seq);
+/* Copy a sequence's table into out[cap]; returns its number of blocks, or a
+ * negative status (PKV_ERR_CAPACITY if cap is too small). */
+int pkv_bm_block_table(const pkv_block_manager* bm, int32_t seq, int32_t* out, int32_t cap);
+/* Rows of a batch: tables[n][max_blocks] (-1 padded) and context_lens[n]. */
+int pkv_bm_export(const pkv_block_manager* bm, const int32_t* seqs, int32_t n, int32_t* tables,
+                  int32_t max_blocks, int32_t* context_lens);
+int pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
+int pkv_bm_num_free(const pkv_block_manager* bm);
+/* Copy the free list (front first) into out[cap]; returns its length. */
+int pkv_bm_free_list(const pkv_block_manager* bm, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,28 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of libpkv.so (C ABI declared in include/pkv.h).  The
+functions here only marshal arguments: every step of the decode path runs in
+the library's HIP kernels.  torch is used for device memory and streams.
+
+If libpkv.so has not been built, importing this package raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._lib import LIB_PATH, PkvError, check, lib
+from .ops import (
+    BlockManager,
+    copy_blocks,
+    gather_kv,
+    paged_attention_decode,
+    reshape_and_cache,
+    workspace_bytes,
+)
+
+__all__ = [
+    "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "gather_kv",
+    "paged_attention_decode", "reshape_and_cache", "workspace_bytes",
+]

@@ -1,0 +1,252 @@
+// C ABI of libpkv: argument checks, split-K planning and kernel dispatch.
+// Nothing here touches device memory; every device pointer is handed to a
+// kernel launched on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pkv.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+// Default split-K partition (tokens) when the caller asks for automatic.
+constexpr int kAutoPartitionValu = 256;
+constexpr int kAutoPartitionMfma = 512;
+
+int dtype_bytes(pkv_dtype dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
+
+struct Plan {
+  int kernel;
+  int32_t part_blocks;
+  int32_t max_parts;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, int32_t max_context_len, pkv_dtype dtype,
+              const pkv_attn_options* opts, Plan* plan) {
+  if (dtype_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const bool sixteen_bit = dtype != PKV_F32;
+  const bool mfma_group = group == 4 || group == 8 || group == 16;
+  const bool valu_group = group == 1 || group == 2 || group == 4 || group == 8;
+  int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
+  if (kernel == PKV_KERNEL_AUTO) kernel = (sixteen_bit && mfma_group) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
+  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group)) return PKV_ERR_UNSUPPORTED;
+  if (kernel == PKV_KERNEL_VALU && !valu_group) return PKV_ERR_UNSUPPORTED;
+  if (kernel != PKV_KERNEL_MFMA && kernel != PKV_KERNEL_VALU) return PKV_ERR_SHAPE;
+
+  // Partition boundaries must fall on block boundaries, and on 32-token
+  // chunk boundaries for the MFMA kernel.
+  const int32_t align = kernel == PKV_KERNEL_MFMA ? (block_size > 32 ? block_size : 32) : block_size;
+  int32_t part = opts ? opts->partition_size : 0;
+  if (part < 0) return PKV_ERR_SHAPE;
+  if (part > 0 && part % align) return PKV_ERR_SHAPE;
+  if (part == 0) part = kernel == PKV_KERNEL_MFMA ? kAutoPartitionMfma : kAutoPartitionValu;
+  part = (int32_t)round_up(part, align);
+
+  const int64_t ctx_blocks = ((int64_t)max_context_len + block_size - 1) / block_size;
+  if ((int64_t)max_context_len <= part) {
+    plan->part_blocks = (int32_t)(ctx_blocks > 0 ? ctx_blocks : 1);
+    plan->max_parts = 1;
+  } else {
+    plan->part_blocks = part / block_size;
+    plan->max_parts = (int32_t)((ctx_blocks + plan->part_blocks - 1) / plan->part_blocks);
+  }
+  if ((int64_t)num_seqs * num_kv_heads * plan->max_parts > kMaxGrid) return PKV_ERR_SHAPE;
+  plan->kernel = kernel;
+  if (plan->max_parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan->max_parts;
+    plan->ws_o_bytes = round_up(rows * head_dim * sizeof(float), 256);
+    plan->ws_bytes = plan->ws_o_bytes + round_up(rows * 2 * sizeof(float), 256);
+  } else {
+    plan->ws_o_bytes = 0;
+    plan->ws_bytes = 0;
+  }
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_str(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid or inconsistent size";
+    case PKV_ERR_DTYPE: return "unknown dtype";
+    case PKV_ERR_UNSUPPORTED: return "no kernel for this combination";
+    case PKV_ERR_ALIGN: return "data pointer not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_NO_BLOCKS: return "block pool exhausted";
+    case PKV_ERR_STATE: return "invalid block manager state or sequence";
+    case PKV_ERR_CAPACITY: return "output buffer too small";
+    default: return "unknown status";
+  }
+}
+
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t max_context_len,
+                                           pkv_dtype dtype, const pkv_attn_options* opts) {
+  Plan plan;
+  if (make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, dtype,
+                opts, &plan) != PKV_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int32_t block_size, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t num_blocks, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, const pkv_attn_options* opts,
+                               void* stream) {
+  Plan plan;
+  const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, dtype, opts, &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGN;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  }
+
+  pkv::AttnParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.ws_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  p.ws_ml = plan.ws_bytes
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_bytes)
+                : nullptr;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.num_blocks = num_blocks;
+  p.part_blocks = plan.part_blocks;
+  p.max_parts = plan.max_parts;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int group = num_q_heads / num_kv_heads;
+  if (opts && opts->main_begin_event) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s) != hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
+  hipError_t err = hipSuccess;
+  const bool have = plan.kernel == PKV_KERNEL_MFMA
+                        ? pkv::launch_attention_mfma(p, dtype, head_dim, block_size, group, s, &err)
+                        : pkv::launch_attention_valu(p, dtype, head_dim, block_size, group, s, &err);
+  if (!have) return PKV_ERR_UNSUPPORTED;
+  if (err != hipSuccess) return PKV_ERR_LAUNCH;
+  if (opts && opts->main_end_event) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->main_end_event), s) != hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
+  if (plan.max_parts > 1) {
+    if (!pkv::launch_attention_reduce(p, dtype, head_dim, block_size, s, &err))
+      return PKV_ERR_UNSUPPORTED;
+    if (err != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          pkv_dtype dtype, void* stream) {
+  const int es = dtype_bytes(dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGN;
+  if ((int64_t)num_tokens * num_kv_heads * head_dim * es / 16 / 256 >= kMaxGrid) return PKV_ERR_SHAPE;
+  return launch_status(pkv::launch_reshape_and_cache(
+      k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim * es, block_size,
+      num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, int32_t num_pairs,
+                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim, int32_t num_blocks,
+                    pkv_dtype dtype, void* stream) {
+  const int es = dtype_bytes(dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs) return PKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_ALIGN;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * es;
+  if ((int64_t)num_pairs * 2 * ((block_bytes + 16383) / 16384) > kMaxGrid) return PKV_ERR_SHAPE;
+  return launch_status(pkv::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs,
+                                               block_bytes, num_blocks,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int pkv_gather_kv(void* dst, const void* cache, const int32_t* block_tables,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                  int32_t max_context_len, int32_t kv_head, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks, pkv_dtype dtype,
+                  void* stream) {
+  const int es = dtype_bytes(dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0 || num_kv_heads <= 0 ||
+      kv_head < 0 || kv_head >= num_kv_heads || head_dim <= 0 || block_size <= 0 ||
+      num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_context_len == 0) return PKV_OK;
+  if (!dst || !cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (!aligned16(dst) || !aligned16(cache)) return PKV_ERR_ALIGN;
+  if ((int64_t)num_seqs * max_context_len * head_dim * es / 16 / 256 >= kMaxGrid) return PKV_ERR_SHAPE;
+  return launch_status(pkv::launch_gather_kv(dst, cache, block_tables, context_lens, num_seqs,
+                                             max_blocks_per_seq, max_context_len, kv_head,
+                                             num_kv_heads, head_dim * es, block_size, num_blocks,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

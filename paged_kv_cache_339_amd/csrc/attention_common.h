@@ -1,0 +1,109 @@
+// Pieces shared by the two decode-attention kernels (vector-ALU and MFMA)
+// and the split-K reduce: per-sequence bookkeeping and the epilogue that
+// merges the waves of a workgroup and stores either the final row or a
+// partition's partial result.
+//
+// Online softmax state, per query head, kept in log2 units: m = running max
+// of scale*log2(e)*<q,k_t>, l = sum_t 2^(x_t - m), o = sum_t 2^(x_t - m) v_t.
+// Two states merge as m = max(m1, m2), l = l1 a1 + l2 a2, o = o1 a1 + o2 a2
+// with ai = 2^(mi - m); a state that has seen no token has m = -inf, l = 0.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+struct SeqWork {
+  int L;        // tokens attended
+  int nblk;     // blocks those tokens occupy
+  int nparts;   // split-K partitions of the sequence
+  bool bad;     // context length outside what the table / launch covers
+};
+
+__device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
+  SeqWork w;
+  const int raw = p.context_lens[s];
+  w.bad = raw < 0 || raw > p.max_context_len ||
+          (int64_t)raw > (int64_t)p.max_blocks_per_seq * B;
+  w.L = w.bad ? 0 : raw;
+  w.nblk = (w.L + B - 1) / B;
+  w.nparts = (w.nblk + p.part_blocks - 1) / p.part_blocks;
+  return w;
+}
+
+// Safe reference point for 2^(x - m) when m may be -inf.
+__device__ __forceinline__ float softmax_ref(float m) { return m == -INFINITY ? 0.f : m; }
+
+// Linear workgroup index -> (sequence, kv head, partition); sequences vary
+// fastest, so workgroups that start together cover the same heads and
+// positions of neighbouring sequences.
+struct WorkItem { int s, h, part; };
+
+__device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
+  int lin = blockIdx.x;
+  WorkItem it;
+  it.s = lin % p.num_seqs;
+  lin /= p.num_seqs;
+  it.h = lin % p.num_kv_heads;
+  it.part = lin / p.num_kv_heads;
+  return it;
+}
+
+// Rows that cannot be computed (data error) become NaN; empty sequences 0.
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void fill_rows(const AttnParams& p, int s, int h, float value) {
+  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
+    const int g = idx / D, d = idx % D;
+    store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + h * G + g) * D + d, value);
+  }
+}
+
+// LDS staging for the cross-wave merge.
+template <int D, int G, int NW>
+struct MergeSmem {
+  float o[NW][G][D];
+  float m[NW][G];
+  float l[NW][G];
+  int bad[NW];
+};
+
+// After every wave has put its (m, l, o) for the G heads into `sm`: merge the
+// waves and store.  A sequence with one partition gets its final output row;
+// otherwise the partition's normalised output and (m, l) go to the
+// workspace for the reduce kernel.
+template <int DT, int D, int G, int NW>
+__device__ __forceinline__ void merge_and_store(const AttnParams& p, const MergeSmem<D, G, NW>& sm,
+                                                int s, int h, int part, int nparts) {
+  bool bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) bad |= sm.bad[w] != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int g = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
+    const float ref = softmax_ref(M);
+    float tot = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = fast_exp2(sm.m[w][g] - ref);
+      tot = fmaf(sm.l[w][g], a, tot);
+      o = fmaf(sm.o[w][g][d], a, o);
+    }
+    const float r = bad ? __builtin_nanf("") : o / tot;
+    const int hq = h * G + g;
+    if (nparts == 1) {
+      store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + hq) * D + d, r);
+    } else {
+      const size_t slot = ((size_t)s * p.num_q_heads + hq) * p.max_parts + part;
+      p.ws_o[slot * D + d] = r;
+      if (d == 0) {
+        p.ws_ml[slot * 2] = M;
+        p.ws_ml[slot * 2 + 1] = bad ? __builtin_nanf("") : tot;
+      }
+    }
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,278 @@
+// Paged decode attention for grouped-query heads on the matrix cores.
+//
+// When G query heads share one KV head (heads sharing one set of keys and
+// values, systemdesign.academy glossary "Paged Attention"), each key/value
+// tile is used G times, and the two products per 32-token chunk are small
+// dense contractions:
+//     scores^T [32 tok x 16]  = K [32 tok x D] * Q^T [D x 16]
+//     out^T    [D x 16]      += V^T [D x 32 tok] * P^T [32 tok x 16]
+// with the G heads padded to the 16 columns of v_mfma_f32_16x16x32_{bf16,f16}
+// (fp32 accumulate).  Keys and values are still read once, through the
+// block table, exactly as in the vector-ALU kernel; the workgroup layout
+// (sequence, KV head, split-K partition) and the epilogue are shared.
+//
+// Operand layouts of the 16x16x32 MFMA (lane l, r = l % 16, q = l / 16):
+//   A (16 x 32): lane holds A[r][8q .. 8q+7]
+//   B (32 x 16): lane holds B[8q .. 8q+7][r]
+//   C (16 x 16): lane holds C[4q + i][r], i = 0..3
+// The contraction index of a product may be permuted freely as long as A
+// and B agree, and so may the rows of A; both freedoms are used so that
+// every lane loads whole 16-byte runs and no data crosses lanes:
+//  * score product: A row R of output tile t is token 8(R/4) + 4t + R%4 and
+//    the contraction index k of k-step s is element 32s + k of head_dim;
+//    lane (r, q) thus ends up with the scores of head r for the eight
+//    consecutive tokens 8q .. 8q+7 of the chunk.
+//  * value product: lane (r, q) loads tokens 8q .. 8q+7, elements
+//    [DPL r, DPL r + DPL) of head_dim (DPL = D/16); an 8x8 transpose of
+//    16-bit values inside the lane (v_perm_b32) gives, for each n < DPL, the
+//    A operand row "element DPL r + n over those tokens"; the B operand is
+//    the lane's own eight softmax weights.  Output tile n then holds, in
+//    lane (r, q), head r at elements DPL(4q + i) + n.
+#include "attention_common.h"
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT> struct Mfma;
+
+template <> struct Mfma<PKV_BF16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
+                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_bf16(x); }
+};
+
+template <> struct Mfma<PKV_F16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
+                                                  __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_f16(x); }
+};
+
+template <int DPL> struct VRow;
+template <> struct VRow<8> {
+  typedef u32x4 type;
+  static __device__ __forceinline__ type load(const char* p) { return load16(p); }
+  static __device__ __forceinline__ type zero() { return u32x4{0, 0, 0, 0}; }
+};
+template <> struct VRow<4> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type load(const char* p) {
+    return *reinterpret_cast<const u32x2*>(p);
+  }
+  static __device__ __forceinline__ type zero() { return u32x2{0, 0}; }
+};
+
+template <int DT, int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(AttnParams p) {
+  constexpr int ES = 2;
+  constexpr int KS = D / 32;      // k-steps of the score product
+  constexpr int DPL = D / 16;     // value elements per lane per token
+  constexpr int CH = 32;          // tokens per chunk
+  static_assert(G >= 1 && G <= 16, "query group must fit 16 MFMA columns");
+  static_assert(B >= 8, "8 consecutive tokens of a lane must share a block");
+  using Ops = Mfma<DT>;
+  using VR = VRow<DPL>;
+
+  __shared__ MergeSmem<D, G, NW> sm;
+
+  const WorkItem it = work_item(p);
+  const SeqWork sw = seq_work(p, it.s, B);
+  if (sw.bad) {
+    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
+    return;
+  }
+  if (sw.L == 0) {
+    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, 0.f);
+    return;
+  }
+  if (it.part >= sw.nparts) return;
+
+  const int lane = lane_id(), w = wave_id();
+  const int r = lane & 15, q = lane >> 4;
+  const int Hkv = p.num_kv_heads, L = sw.L, N = p.num_blocks;
+
+  u32x4 qb[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = (r < G) ? load16(qrow + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 o[DPL];
+#pragma unroll
+  for (int n = 0; n < DPL; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  int bad = 0;
+
+  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache);
+  const int tb = it.part * p.part_blocks * B;
+  const int te = min(L, tb + p.part_blocks * B);
+  const int nch = (te - tb + CH - 1) / CH;
+
+  for (int ci = w; ci < nch; ci += NW) {
+    const int c0 = tb + ci * CH;
+
+    // Keys: lane (r, q) loads token 8(r/4) + 4t + r%4 of the chunk for t = 0, 1,
+    // head_dim elements 32s + 8q .. +8 for every k-step s.
+    u32x4 kr[2][KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int tok = c0 + 8 * (r >> 2) + 4 * t + (r & 3);
+      bool ok = tok < L;
+      int blk = ok ? table[tok / B] : 0;
+      if (ok && (unsigned)blk >= (unsigned)N) {
+        bad = 1;
+        ok = false;
+      }
+      const char* kp = kbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tok % B) * D + 8 * q) * ES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = ok ? load16(kp + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+    }
+    // Values: tokens 8q .. 8q+7 (one block), elements DPL r .. DPL r + DPL.
+    typename VR::type vr[8];
+    {
+      const int tv0 = c0 + 8 * q;
+      bool ok = tv0 < L;
+      int blk = ok ? table[tv0 / B] : 0;
+      if (ok && (unsigned)blk >= (unsigned)N) {
+        bad = 1;
+        ok = false;
+      }
+      const char* vp = vbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tv0 % B) * D + DPL * r) * ES;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vr[j] = (ok && tv0 + j < L) ? VR::load(vp + (size_t)j * D * ES) : VR::zero();
+    }
+
+    // Scores of head r for tokens c0 + 8q + j, j = 4t + i.
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = Ops::mma(kr[t][ks], qb[ks], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i] * p.scale_log2;
+    }
+    if (c0 + CH > L) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + 8 * q + j >= L) sc[j] = -INFINITY;
+    }
+
+    float cm = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
+    cm = fmaxf(cm, shfl_xor_f(cm, 16));
+    cm = fmaxf(cm, shfl_xor_f(cm, 32));
+    const float mn = fmaxf(m, cm);
+    const float ref = softmax_ref(mn);
+    const float alpha = fast_exp2(m - ref);
+    m = mn;
+
+    // Weights rounded to the operand format; the sum uses the rounded values.
+    u32x4 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = Ops::narrow(fast_exp2(sc[2 * k] - ref));
+      const uint32_t hi = Ops::narrow(fast_exp2(sc[2 * k + 1] - ref));
+      pb[k] = lo | (hi << 16);
+      ps += widen_half<DT>(pb[k], false) + widen_half<DT>(pb[k], true);
+    }
+    l = fmaf(l, alpha, ps);
+
+#pragma unroll
+    for (int n = 0; n < DPL; ++n) {
+      u32x4 a;
+      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = __builtin_amdgcn_perm(vr[2 * k + 1][n >> 1], vr[2 * k][n >> 1], sel);
+      o[n] *= alpha;
+      o[n] = Ops::mma(a, pb, o[n]);
+    }
+  }
+
+  l += shfl_xor_f(l, 16);
+  l += shfl_xor_f(l, 32);
+  const int any_bad = __any(bad);
+
+  if (r < G) {
+#pragma unroll
+    for (int n = 0; n < DPL; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.o[w][r][DPL * (4 * q + i) + n] = o[n][i];
+    if (q == 0) {
+      sm.m[w][r] = m;
+      sm.l[w][r] = l;
+    }
+  }
+  if (lane == 0) sm.bad[w] = any_bad;
+  __syncthreads();
+  merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMfmaWaves = 4;
+
+template <int DT, int D, int B, int G>
+hipError_t launch_mfma(const AttnParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, B, G, kMfmaWaves>), grid, dim3(kMfmaWaves * kWave), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D, int B>
+bool by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
+  switch (G) {
+    case 4: *e = launch_mfma<DT, D, B, 4>(p, st); return true;
+    case 8: *e = launch_mfma<DT, D, B, 8>(p, st); return true;
+    case 16: *e = launch_mfma<DT, D, B, 16>(p, st); return true;
+    default: return false;
+  }
+}
+
+template <int DT, int D>
+bool by_block(const AttnParams& p, int B, int G, hipStream_t st, hipError_t* e) {
+  switch (B) {
+    case 8: return by_group<DT, D, 8>(p, G, st, e);
+    case 16: return by_group<DT, D, 16>(p, G, st, e);
+    case 32: return by_group<DT, D, 32>(p, G, st, e);
+    case 64: return by_group<DT, D, 64>(p, G, st, e);
+    default: return false;
+  }
+}
+
+template <int DT>
+bool by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipError_t* e) {
+  switch (D) {
+    case 64: return by_block<DT, 64>(p, B, G, st, e);
+    case 128: return by_block<DT, 128>(p, B, G, st, e);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
+                           int group, hipStream_t stream, hipError_t* err) {
+  switch (dt) {
+    case PKV_F16: return by_dim<PKV_F16>(p, head_dim, block_size, group, stream, err);
+    case PKV_BF16: return by_dim<PKV_BF16>(p, head_dim, block_size, group, stream, err);
+    default: return false;
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,252 @@
+// Paged decode attention on the vector ALUs (few query heads per KV head).
+//
+// Block-wise attention through the block table ("pagedattention vllm"
+// glossary, Attention Computation: Block-Wise Attention, Address
+// Translation): each workgroup owns one (sequence, KV head, split-K
+// partition); its waves take the partition's blocks in turn, translate the
+// logical block to the physical one through the table, load the key and
+// value tile of that (block, head) straight into registers with 16-byte
+// loads, and fold them into a per-lane online softmax.
+//
+// Lane mapping for a [B, D] tile of one block and head (rows contiguous):
+// a token row of D*bytes is split over LPT lanes holding 16 bytes each, so
+// one wave-wide load covers TPW = 64/LPT consecutive rows (1 KiB,
+// contiguous).  Lane `grp = lane / LPT` owns rows grp, grp+TPW, ... of every
+// tile it visits; the <q, k> partial dots are summed across the LPT lanes of
+// a row with DPP, the P*V products accumulate in place for the lane's
+// 16-byte slice of head_dim.  Lane groups and waves are merged at the end.
+#include "attention_common.h"
+
+namespace pkv {
+
+template <int DT, int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
+  constexpr int ES = Format<DT>::kBytes;
+  constexpr int EPL = 16 / ES;       // elements per lane per load
+  constexpr int LPT = D / EPL;       // lanes per token row
+  constexpr int TPW = kWave / LPT;   // token rows per wave-wide load
+  constexpr int NL = B / TPW;        // loads per tile per lane
+  static_assert(LPT >= 1 && LPT <= kWave && B % TPW == 0, "tile does not map onto a wave");
+
+  __shared__ MergeSmem<D, G, NW> sm;
+
+  const WorkItem it = work_item(p);
+  const SeqWork sw = seq_work(p, it.s, B);
+  if (sw.bad) {
+    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
+    return;
+  }
+  if (sw.L == 0) {
+    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, 0.f);
+    return;
+  }
+  if (it.part >= sw.nparts) return;
+
+  const int lane = lane_id(), w = wave_id();
+  const int grp = lane / LPT, sub = lane % LPT;
+  const int Hkv = p.num_kv_heads;
+
+  // Query rows of the G heads that share this KV head, pre-scaled.
+  float qf[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * ES;
+    widen16<DT>(load16(qrow), qf[g]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache);
+  const int b0 = it.part * p.part_blocks;
+  const int b1 = min(sw.nblk, b0 + p.part_blocks);
+  const int tail = sw.L - (sw.nblk - 1) * B;      // tokens in the last block, 1..B
+  int bad = 0;
+
+  for (int b = b0 + w; b < b1; b += NW) {
+    const int phys = table[b];
+    if ((unsigned)phys >= (unsigned)p.num_blocks) {
+      bad = 1;
+      continue;
+    }
+    const size_t lane_off = (((size_t)phys * Hkv + it.h) * B + grp) * D + sub * EPL;
+    const char* kt = kbase + lane_off * ES;
+    const char* vt = vbase + lane_off * ES;
+    const int valid = (b == sw.nblk - 1) ? tail : B;
+
+    u32x4 kr[NL], vr[NL];
+    if (valid == B) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) kr[i] = load16(kt + (size_t)i * TPW * D * ES);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) vr[i] = load16(vt + (size_t)i * TPW * D * ES);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        kr[i] = u32x4{0, 0, 0, 0};
+        vr[i] = u32x4{0, 0, 0, 0};
+        if (i * TPW + grp < valid) {
+          kr[i] = load16(kt + (size_t)i * TPW * D * ES);
+          vr[i] = load16(vt + (size_t)i * TPW * D * ES);
+        }
+      }
+    }
+
+    float sc[G][NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float kf[EPL];
+      widen16<DT>(kr[i], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(qf[g][e], kf[e], a);
+        sc[g][i] = group_sum<LPT>(a);
+      }
+    }
+    if (valid != B) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (i * TPW + grp >= valid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) sc[g][i] = -INFINITY;
+        }
+    }
+
+    float pr[G][NL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = sc[g][0];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[g][i]);
+      const float mn = fmaxf(m[g], mx);
+      const float ref = softmax_ref(mn);
+      const float alpha = fast_exp2(m[g] - ref);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        pr[g][i] = fast_exp2(sc[g][i] - ref);
+        ps += pr[g][i];
+      }
+      l[g] = fmaf(l[g], alpha, ps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+      m[g] = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[EPL];
+      widen16<DT>(vr[i], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[g][i], vf[e], acc[g][e]);
+    }
+  }
+
+  // Merge the TPW lane groups of the wave (lanes sub, sub+LPT, ...).
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m2 = shfl_xor_f(m[g], off);
+      const float l2 = shfl_xor_f(l[g], off);
+      const float mn = fmaxf(m[g], m2);
+      const float ref = softmax_ref(mn);
+      const float a1 = fast_exp2(m[g] - ref), a2 = fast_exp2(m2 - ref);
+      l[g] = l[g] * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * a1 + shfl_xor_f(acc[g][e], off) * a2;
+      m[g] = mn;
+    }
+  }
+
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm.o[w][g][sub * EPL + e] = acc[g][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      sm.m[w][g] = m[g];
+      sm.l[w][g] = l[g];
+    }
+    sm.bad[w] = bad;
+  }
+  __syncthreads();
+  merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
+}
+
+// ---------------------------------------------------------------------------
+// Instantiation and dispatch.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kValuWaves = 4;
+
+template <int DT, int D, int B, int G>
+hipError_t launch_valu(const AttnParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
+  hipLaunchKernelGGL((attn_valu_kernel<DT, D, B, G, kValuWaves>), grid, dim3(kValuWaves * kWave), 0,
+                     st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D, int B>
+bool by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
+  switch (G) {
+    case 1: *e = launch_valu<DT, D, B, 1>(p, st); return true;
+    case 2: *e = launch_valu<DT, D, B, 2>(p, st); return true;
+    case 4: *e = launch_valu<DT, D, B, 4>(p, st); return true;
+    case 8: *e = launch_valu<DT, D, B, 8>(p, st); return true;
+    default: return false;
+  }
+}
+
+template <int DT, int D>
+bool by_block(const AttnParams& p, int B, int G, hipStream_t st, hipError_t* e) {
+  switch (B) {
+    case 8: return by_group<DT, D, 8>(p, G, st, e);
+    case 16: return by_group<DT, D, 16>(p, G, st, e);
+    case 32: return by_group<DT, D, 32>(p, G, st, e);
+    case 64: return by_group<DT, D, 64>(p, G, st, e);
+    default: return false;
+  }
+}
+
+template <int DT>
+bool by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipError_t* e) {
+  switch (D) {
+    case 64: return by_block<DT, 64>(p, B, G, st, e);
+    case 128: return by_block<DT, 128>(p, B, G, st, e);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
+                           int group, hipStream_t stream, hipError_t* err) {
+  switch (dt) {
+    case PKV_F32: return by_dim<PKV_F32>(p, head_dim, block_size, group, stream, err);
+    case PKV_F16: return by_dim<PKV_F16>(p, head_dim, block_size, group, stream, err);
+    case PKV_BF16: return by_dim<PKV_BF16>(p, head_dim, block_size, group, stream, err);
+    default: return false;
+  }
+}
+
+}  // namespace pkv

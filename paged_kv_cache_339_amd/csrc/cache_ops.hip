@@ -1,0 +1,122 @@
+// Byte-moving kernels of the KV block pool: the new-token scatter
+// (reshape_and_cache), the copy-on-write block copy (copy_blocks) and a
+// gather through the block tables used to check addressing.  All of them
+// move 16-byte units with vector loads and stores; none looks at values.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+// One thread per 16-byte chunk of a (token, head) row.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t total,
+    int32_t num_kv_heads, int32_t chunks, int32_t block_size, int64_t num_slots) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % chunks);
+  const int64_t row = idx / chunks;           // token * Hkv + head
+  const int h = (int)(row % num_kv_heads);
+  const int64_t i = row / num_kv_heads;
+  const int32_t slot = slot_mapping[i];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int64_t blk = slot / block_size, off = slot % block_size;
+  const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
+  const size_t src = ((size_t)row * chunks + c) * 16;
+  store16(k_cache + dst, load16(k + src));
+  store16(v_cache + dst, load16(v + src));
+}
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                                    int32_t num_blocks, hipStream_t stream) {
+  const int32_t chunks = row_bytes / 16;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  hipLaunchKernelGGL(reshape_and_cache_kernel, grid, dim3(256), 0, stream,
+                     static_cast<const char*>(k), static_cast<const char*>(v),
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), slot_mapping, total,
+                     num_kv_heads, chunks, block_size, (int64_t)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+// Each workgroup copies one 16 KiB piece of one block of one cache.
+constexpr int kCopyPiece = 16384;
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache,
+                                                          char* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t block_bytes, int32_t pieces,
+                                                          int32_t num_blocks) {
+  const int pair = blockIdx.x / (2 * pieces);
+  const int rest = blockIdx.x % (2 * pieces);
+  const int which = rest / pieces, piece = rest % pieces;
+  const int32_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+  char* base = which ? v_cache : k_cache;
+  const char* from = base + (size_t)src * block_bytes;
+  char* to = base + (size_t)dst * block_bytes;
+  const int64_t begin = (int64_t)piece * kCopyPiece;
+  u32x4 buf[kCopyPiece / (256 * 16)];
+#pragma unroll
+  for (int j = 0; j < kCopyPiece / (256 * 16); ++j) {
+    const int64_t off = begin + ((int64_t)j * 256 + threadIdx.x) * 16;
+    if (off < block_bytes) buf[j] = load16(from + off);
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyPiece / (256 * 16); ++j) {
+    const int64_t off = begin + ((int64_t)j * 256 + threadIdx.x) * 16;
+    if (off < block_bytes) store16(to + off, buf[j]);
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int32_t pieces = (int32_t)((block_bytes + kCopyPiece - 1) / kCopyPiece);
+  const dim3 grid((unsigned)((int64_t)num_pairs * 2 * pieces));
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), pairs, block_bytes, pieces, num_blocks);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte chunk of dst[s][t][:].
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    char* __restrict__ dst, const char* __restrict__ cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, int64_t total, int32_t max_blocks, int32_t max_len,
+    int32_t kv_head, int32_t num_kv_heads, int32_t chunks, int32_t block_size,
+    int32_t num_blocks) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % chunks);
+  const int64_t row = idx / chunks;          // s * max_len + t
+  const int t = (int)(row % max_len);
+  const int64_t s = row / max_len;
+  const int32_t L = lens[s];
+  if (t >= L || t / block_size >= max_blocks) return;
+  const int32_t blk = tables[s * max_blocks + t / block_size];
+  if ((unsigned)blk >= (unsigned)num_blocks) return;
+  const size_t src =
+      ((((size_t)blk * num_kv_heads + kv_head) * block_size + t % block_size) * chunks + c) * 16;
+  store16(dst + ((size_t)row * chunks + c) * 16, load16(cache + src));
+}
+
+hipError_t launch_gather_kv(void* dst, const void* cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, int32_t kv_head,
+                            int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                            int32_t num_blocks, hipStream_t stream) {
+  const int32_t chunks = row_bytes / 16;
+  const int64_t total = (int64_t)num_seqs * max_context_len * chunks;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  hipLaunchKernelGGL(gather_kv_kernel, grid, dim3(256), 0, stream, static_cast<char*>(dst),
+                     static_cast<const char*>(cache), block_tables, context_lens, total,
+                     max_blocks_per_seq, max_context_len, kv_head, num_kv_heads, chunks,
+                     block_size, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Everything the decode-attention kernels read.  Sizes are validated by the
+// C ABI before a launch.
+struct AttnParams {
+  void* out;                  // [S, Hq, D]
+  const void* q;              // [S, Hq, D]
+  const void* k_cache;        // [N, Hkv, B, D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [S, M]
+  const int32_t* context_lens;  // [S]
+  float* ws_o;                // [S, Hq, P, D] partition outputs, normalised
+  float* ws_ml;               // [S, Hq, P, 2]  (running max in log2 units, sum)
+  float scale_log2;           // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int32_t num_blocks;
+  int32_t part_blocks;        // blocks per split-K partition
+  int32_t max_parts;          // partitions per sequence covered by the grid
+};
+
+// Returns false when no kernel instance exists for the combination.
+bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
+                           int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
+                           int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_reduce(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
+                             hipStream_t stream, hipError_t* err);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                                    int32_t num_blocks, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, int32_t num_blocks, hipStream_t stream);
+hipError_t launch_gather_kv(void* dst, const void* cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, int32_t kv_head,
+                            int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
+                            int32_t num_blocks, hipStream_t stream);
+
+}  // namespace pkv

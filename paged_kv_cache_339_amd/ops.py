@@ -1,0 +1,240 @@
+"""Argument marshalling from torch tensors / numpy arrays to the C ABI.
+
+Device tensors must be contiguous and on the GPU; the stream defaults to
+torch's current stream.  Nothing here computes: each call is one library
+call (plus, at most, a workspace allocation when the caller passes none).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import KERNELS, AttnOptions, PkvError, c_i32p, check, lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _options(partition_size, kernel, main_events):
+    ev0, ev1 = (None, None) if main_events is None else main_events
+    return AttnOptions(int(partition_size), KERNELS[kernel],
+                       None if ev0 is None else ctypes.c_void_p(int(ev0)),
+                       None if ev1 is None else ctypes.c_void_p(int(ev1)))
+
+
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                    dtype_code_, partition_size=0, kernel="auto") -> int:
+    opts = _options(partition_size, kernel, None)
+    return int(lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                       block_size, max_context_len, dtype_code_,
+                                                       ctypes.byref(opts)))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                           num_kv_heads, max_context_len, partition_size=0, kernel="auto",
+                           workspace=None, stream=None, main_events=None):
+    """out[s, j] = softmax(scale * q[s, j] K_s^T) V_s through the block tables.
+
+    q, out: [S, Hq, D]; k_cache, v_cache: [N, Hkv, B, D]; block_tables int32
+    [S, M]; context_lens int32 [S] (device); max_context_len: host int >=
+    every context length.  `workspace`: optional uint8 device tensor of at
+    least workspace_bytes(...) bytes."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("k_cache and v_cache must match each other and q's dtype")
+    if D2 != D or B != block_size or Hkv != num_kv_heads:
+        raise ValueError("cache shape disagrees with head_dim / block_size / num_kv_heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and context_lens [S]")
+    code = dtype_code(q)
+    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opts = _options(partition_size, kernel, main_events)
+    st = lib.pkv_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), B, Hkv, S, Hq, D, block_tables.shape[1], int(max_context_len), N, code,
+        ws_ptr, ws_len, ctypes.byref(opts), _stream(stream))
+    check(st, "paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """k_cache[slot // B, :, slot % B] = k[i] (and v) for every slot >= 0."""
+    torch = _torch()
+    T, Hkv, D = k.shape
+    N, Hkv2, B, D2 = k_cache.shape
+    if tuple(v.shape) != (T, Hkv, D) or (Hkv2, D2) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between new tokens and caches")
+    if not (k.dtype == v.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = lib.pkv_reshape_and_cache(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, B, N,
+                                   dtype_code(k), _stream(stream))
+    check(st, "reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
+    """Block dst of both caches becomes a copy of block src, for each pair."""
+    torch = _torch()
+    N, Hkv, B, D = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [num_pairs, 2]")
+    n = src_dst_pairs.shape[0]
+    st = lib.pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                             _dev(src_dst_pairs, "src_dst_pairs", torch.int32) if n else None,
+                             n, Hkv, B, D, N, dtype_code(k_cache), _stream(stream))
+    check(st, "copy_blocks")
+
+
+def gather_kv(cache, block_tables, context_lens, kv_head, max_context_len, out=None, stream=None):
+    """Contiguous [S, max_context_len, D] copy of one KV head through the tables
+    (rows past a sequence's length keep out's previous contents; zeros if out is None)."""
+    torch = _torch()
+    N, Hkv, B, D = cache.shape
+    S, M = block_tables.shape
+    if out is None:
+        out = torch.zeros((S, max_context_len, D), dtype=cache.dtype, device=cache.device)
+    st = lib.pkv_gather_kv(_dev(out, "out"), _dev(cache, "cache"), _dev(block_tables, "block_tables", torch.int32),
+                           _dev(context_lens, "context_lens", torch.int32), S, M, int(max_context_len),
+                           int(kv_head), Hkv, D, B, N, dtype_code(cache), _stream(stream))
+    check(st, "gather_kv")
+    return out
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr, arr.ctypes.data_as(c_i32p)
+
+
+class BlockManager:
+    """Host block manager of libpkv (free list, refcounts, tables, CoW)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, free_order=None):
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        keep = None
+        ptr = None
+        if free_order is not None:
+            keep, ptr = _i32(free_order)
+            if keep.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+        self._h = lib.pkv_bm_create(num_blocks, block_size, max_seqs, ptr)
+        if not self._h:
+            raise ValueError("pkv_bm_create rejected its arguments")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def add_seq(self, seq):
+        check(lib.pkv_bm_add_seq(self._h, seq), "bm_add_seq")
+
+    def fork(self, parent, child):
+        check(lib.pkv_bm_fork(self._h, parent, child), "bm_fork")
+
+    def append(self, seq):
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pkv_bm_append(self._h, seq, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)),
+              "bm_append")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_batch(self, seqs):
+        seqs_a, seqs_p = _i32(seqs)
+        n = len(seqs_a)
+        slots, slots_p = _i32(np.zeros(n))
+        pairs, pairs_p = _i32(np.zeros(2 * max(1, n)))
+        npairs, done = ctypes.c_int32(), ctypes.c_int32()
+        st = lib.pkv_bm_append_batch(self._h, seqs_p, n, slots_p, pairs_p, n, ctypes.byref(npairs),
+                                     ctypes.byref(done))
+        if st != 0:
+            err = PkvError(st, "bm_append_batch")
+            err.num_done = done.value
+            raise err
+        return slots, pairs[: 2 * npairs.value].reshape(-1, 2).copy()
+
+    def free_seq(self, seq):
+        check(lib.pkv_bm_free_seq(self._h, seq), "bm_free_seq")
+
+    def seq_len(self, seq):
+        n = lib.pkv_bm_seq_len(self._h, seq)
+        if n < 0:
+            raise PkvError(n, "bm_seq_len")
+        return n
+
+    def block_table(self, seq):
+        cap = max(1, -(-self.seq_len(seq) // self.block_size))
+        buf, ptr = _i32(np.zeros(cap))
+        n = lib.pkv_bm_block_table(self._h, seq, ptr, cap)
+        if n < 0:
+            raise PkvError(n, "bm_block_table")
+        return buf[:n].tolist()
+
+    def export(self, seqs, max_blocks):
+        seqs_a, seqs_p = _i32(seqs)
+        n = len(seqs_a)
+        tables, tp = _i32(np.zeros((n, max_blocks)))
+        lens, lp = _i32(np.zeros(n))
+        check(lib.pkv_bm_export(self._h, seqs_p, n, tp, max_blocks, lp), "bm_export")
+        return tables, lens
+
+    def refcount(self, block):
+        n = lib.pkv_bm_refcount(self._h, block)
+        if n < 0:
+            raise PkvError(n, "bm_refcount")
+        return n
+
+    def num_free(self):
+        return lib.pkv_bm_num_free(self._h)
+
+    def free_list(self):
+        buf, ptr = _i32(np.zeros(max(1, self.num_blocks)))
+        n = lib.pkv_bm_free_list(self._h, ptr, max(1, self.num_blocks))
+        return buf[:n].tolist()

@@ -73,8 +73,7 @@ def _ceil_div(a: int, b: int) -> int:
 def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
     """Seeded placement.  `lengths` overrides the drawn lengths (edge-case tests)."""
     rng = np.random.default_rng(seed)
-    drawn = draw_lengths(cfg, rng)
-    lens = drawn if lengths is None else np.asarray(lengths, dtype=np.int32)
+    lens = draw_lengths(cfg, rng) if lengths is None else np.asarray(lengths, dtype=np.int32)
     S, B = len(lens), cfg.block_size
     nblk = [_ceil_div(int(L), B) for L in lens]
 

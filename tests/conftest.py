@@ -9,3 +9,15 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: larger CPU cases")
+
+
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if it.get_closest_marker("gpu")]
+    if not gpu_items:
+        return
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        skip = pytest.mark.skip(reason="no GPU visible to torch")
+        for it in gpu_items:
+            it.add_marker(skip)

@@ -1,0 +1,102 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/pkv.h declares, and rejects bad arguments before launching anything.
+Only argument combinations that fail a host check are passed here, so no
+call reaches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_339_amd as pkv
+from paged_kv_cache_339_amd._lib import AttnOptions
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 19
+    raw = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code in range(0, -11, -1):
+        s = pkv.lib.pkv_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert pkv.lib.pkv_status_str(-99).decode() == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every call below fails a host check
+
+
+def decode(**over):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, scale=0.125, B=16, Hkv=2,
+                S=4, Hq=2, D=64, M=4, max_ctx=64, N=32, dtype=0, ws=None, ws_bytes=0, opts=None,
+                stream=None)
+    args.update(over)
+    a = args
+    return pkv.lib.pkv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["tables"], a["lens"],
+                                              a["scale"], a["B"], a["Hkv"], a["S"], a["Hq"], a["D"],
+                                              a["M"], a["max_ctx"], a["N"], a["dtype"], a["ws"],
+                                              a["ws_bytes"], a["opts"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(tables=None), -1), (dict(lens=None), -1),
+    (dict(dtype=7), -3), (dict(D=96), -4), (dict(D=256), -4), (dict(B=12), -4), (dict(B=128), -4),
+    (dict(Hq=3), -2), (dict(Hq=6, Hkv=2), -4), (dict(S=-1), -2), (dict(max_ctx=-5), -2),
+    (dict(M=0), -2), (dict(N=0), -2), (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(q=ctypes.c_void_p(0x1008)), -5), (dict(k=ctypes.c_void_p(0x1004)), -5),
+    (dict(max_ctx=5000), -6),                             # needs a split-K workspace
+    (dict(max_ctx=5000, ws=FAKE, ws_bytes=16), -6),
+])
+def test_decode_rejects(over, status):
+    assert decode(**over) == status
+
+
+def test_decode_mfma_only_for_16_bit_groups():
+    opts = AttnOptions(0, 2, None, None)
+    assert decode(opts=ctypes.byref(opts)) == -4                        # f32, group 1
+    assert decode(opts=ctypes.byref(opts), dtype=2, Hq=16, Hkv=2, max_ctx=5000) == -6  # reaches workspace check
+    bad_part = AttnOptions(40, 0, None, None)
+    assert decode(opts=ctypes.byref(bad_part), max_ctx=5000) == -2     # not a multiple of B
+    bad_mfma_part = AttnOptions(16, 2, None, None)
+    assert decode(opts=ctypes.byref(bad_mfma_part), dtype=2, Hq=16, Hkv=2, max_ctx=5000) == -2
+
+
+def test_empty_batch_is_a_no_op():
+    assert decode(S=0, out=None, q=None) == 0
+
+
+def test_workspace_sizes():
+    ws = pkv.workspace_bytes
+    assert ws(4, 2, 2, 64, 16, 64, 0) == 0                             # one partition
+    n = ws(64, 32, 32, 128, 16, 2048, 1)                                # 256-token default partitions
+    rows = 64 * 32 * 8
+    assert n == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 2 * 4 + 255) // 256 * 256
+    assert ws(64, 32, 32, 128, 16, 2048, 1, partition_size=512) < n
+    assert ws(256, 64, 8, 128, 32, 32768, 2) > 0                        # MFMA, 512-token partitions
+    assert ws(4, 2, 2, 96, 16, 64, 0) == 0                              # invalid -> 0
+
+
+def test_scatter_and_copy_reject():
+    L = pkv.lib
+    assert L.pkv_reshape_and_cache(None, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 16, 32, 0, None) == -1
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 16, 32, 9, None) == -3
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 6, 16, 32, 1, None) == -4
+    assert L.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 64, 16, 32, 0, None) == -2
+    assert L.pkv_reshape_and_cache(FAKE, ctypes.c_void_p(0x1002), FAKE, FAKE, FAKE, 4, 2, 64, 16, 32, 0, None) == -5
+    assert L.pkv_reshape_and_cache(None, None, None, None, None, 0, 2, 64, 16, 32, 0, None) == 0
+    assert L.pkv_copy_blocks(FAKE, FAKE, None, 3, 2, 16, 64, 32, 0, None) == -1
+    assert L.pkv_copy_blocks(FAKE, FAKE, FAKE, -3, 2, 16, 64, 32, 0, None) == -2
+    assert L.pkv_copy_blocks(None, None, None, 0, 2, 16, 64, 32, 0, None) == 0
+    assert L.pkv_gather_kv(FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 2, 2, 64, 16, 32, 0, None) == -2
