@@ -113,9 +113,19 @@ def cpu_baseline(cfg, layout, cpu_seconds: float):
 # ---------------------------------------------------------------------------
 # HIP events on the launch stream (ctypes on the HIP runtime).
 # ---------------------------------------------------------------------------
+def loaded_hip_runtime() -> str:
+    """Path of the HIP runtime already mapped into this process (torch's own
+    copy), so events live in the same runtime as torch's streams."""
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1]
+        if "libamdhip64.so" in path:
+            return path
+    raise RuntimeError("no HIP runtime loaded")
+
+
 class HipEvents:
     def __init__(self):
-        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip = ctypes.CDLL(loaded_hip_runtime())
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]

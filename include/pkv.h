@@ -65,6 +65,10 @@ enum pkv_status {
 /* Human-readable name of a status code (static storage). */
 const char* pkv_status_str(int status);
 
+/* Description of the HIP runtime error behind the last PKV_ERR_LAUNCH
+ * returned on the calling thread ("" if none); valid until the next call. */
+const char* pkv_last_error(void);
+
 /* ------------------------------------------------------------------------ */
 /* Decode attention                                                          */
 /* ------------------------------------------------------------------------ */

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "kernels.h"
 #include "pkv.h"
@@ -88,11 +89,23 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   return PKV_OK;
 }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+thread_local char g_last_error[256] = "";
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s (hipError %d)", hipGetErrorString(e), (int)e);
+  return PKV_ERR_LAUNCH;
+}
+
+// Clear an error left pending by earlier runtime calls of the caller, so the
+// check after a launch reports that launch only.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
 extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error; }
 
 const char* pkv_status_str(int status) {
   switch (status) {
@@ -168,24 +181,25 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / num_kv_heads;
+  clear_pending_error();
   if (opts && opts->main_begin_event) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s) != hipSuccess)
-      return PKV_ERR_LAUNCH;
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
+    if (e != hipSuccess) return launch_status(e);
   }
   hipError_t err = hipSuccess;
   const bool have = plan.kernel == PKV_KERNEL_MFMA
                         ? pkv::launch_attention_mfma(p, dtype, head_dim, block_size, group, s, &err)
                         : pkv::launch_attention_valu(p, dtype, head_dim, block_size, group, s, &err);
   if (!have) return PKV_ERR_UNSUPPORTED;
-  if (err != hipSuccess) return PKV_ERR_LAUNCH;
+  if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_end_event) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->main_end_event), s) != hipSuccess)
-      return PKV_ERR_LAUNCH;
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_end_event), s);
+    if (e != hipSuccess) return launch_status(e);
   }
   if (plan.max_parts > 1) {
     if (!pkv::launch_attention_reduce(p, dtype, head_dim, block_size, s, &err))
       return PKV_ERR_UNSUPPORTED;
-    if (err != hipSuccess) return PKV_ERR_LAUNCH;
+    if (err != hipSuccess) return launch_status(err);
   }
   return PKV_OK;
 }
@@ -204,6 +218,7 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_ALIGN;
   if ((int64_t)num_tokens * num_kv_heads * head_dim * es / 16 / 256 >= kMaxGrid) return PKV_ERR_SHAPE;
+  clear_pending_error();
   return launch_status(pkv::launch_reshape_and_cache(
       k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim * es, block_size,
       num_blocks, static_cast<hipStream_t>(stream)));
@@ -222,6 +237,7 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, 
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_ALIGN;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * es;
   if ((int64_t)num_pairs * 2 * ((block_bytes + 16383) / 16384) > kMaxGrid) return PKV_ERR_SHAPE;
+  clear_pending_error();
   return launch_status(pkv::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs,
                                                block_bytes, num_blocks,
                                                static_cast<hipStream_t>(stream)));
@@ -243,6 +259,7 @@ int pkv_gather_kv(void* dst, const void* cache, const int32_t* block_tables,
   if (!dst || !cache || !block_tables || !context_lens) return PKV_ERR_NULL;
   if (!aligned16(dst) || !aligned16(cache)) return PKV_ERR_ALIGN;
   if ((int64_t)num_seqs * max_context_len * head_dim * es / 16 / 256 >= kMaxGrid) return PKV_ERR_SHAPE;
+  clear_pending_error();
   return launch_status(pkv::launch_gather_kv(dst, cache, block_tables, context_lens, num_seqs,
                                              max_blocks_per_seq, max_context_len, kv_head,
                                              num_kv_heads, head_dim * es, block_size, num_blocks,

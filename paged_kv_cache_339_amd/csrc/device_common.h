@@ -48,7 +48,12 @@ template <int DT>
 __device__ __forceinline__ void widen16(const u32x4& raw, float* f) {
   if constexpr (DT == PKV_F32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, raw[i]);
+    for (int i = 0; i < 4; ++i) {
+      // Copy the element out first: a bit_cast applied directly to an
+      // ext_vector element reads element 0 with this compiler.
+      const uint32_t w = raw[i];
+      f[i] = __builtin_bit_cast(float, w);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
