@@ -26,7 +26,8 @@ class PkvError(RuntimeError):
                          + (f": {detail}" if detail else ""))
 
 
-def _load():
+def load(path: str = LIB_PATH):
+    """ctypes handle of a libpkv build with every prototype set."""
     # torch ships its own HIP runtime (same soname as ROCm's).  Load it first
     # so libpkv binds to the runtime that owns torch's memory and streams;
     # loading libpkv first would put a second HIP runtime in the process.
@@ -34,11 +35,11 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python paged_kv_cache_339_amd/build.py` "
+            f"{path} is missing: build it with `python paged_kv_cache_339_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation.")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     sig = {
         "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pkv_last_error": (ctypes.c_char_p, []),
@@ -73,7 +74,7 @@ def _load():
     return L
 
 
-lib = _load()
+lib = load()
 
 
 def check(status: int, where: str) -> None:

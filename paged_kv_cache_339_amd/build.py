@@ -47,11 +47,11 @@ def sources():
     return out
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+        cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
@@ -62,21 +62,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = True, out: str = LIB, build_dir: str = BUILD,
+          defines=()) -> str:
+    """Compile every source and link `out`.  `defines` are extra -D options
+    (tuning constants of the kernels)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    extra = [f"-D{d}" for d in defines]
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -14,8 +14,16 @@ namespace {
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
 // Default split-K partition (tokens) when the caller asks for automatic.
-constexpr int kAutoPartitionValu = 256;
-constexpr int kAutoPartitionMfma = 512;
+// Automatic split-K partition: the smallest power of two of at least
+// kMinAutoPartition tokens that still leaves about kFillItems
+// (sequence, KV head, partition) work items when every sequence is as long
+// as the longest; an MI355X keeps 1280 of these workgroups resident (256 CUs
+// x 5), and the plan orders them longest first, so the machine stays full
+// and the last items are short.  Measured: fewer, longer partitions beat
+// short ones as soon as there are enough items (no reduce pass, no
+// partial-result traffic).
+constexpr int64_t kFillItems = 2560;
+constexpr int64_t kMinAutoPartition = 1024;
 
 int dtype_bytes(pkv_dtype dt) {
   switch (dt) {
@@ -30,11 +38,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 
+// Workspace layout: [work header][work pairs][partition outputs][partition (m, l)].
 struct Plan {
   int kernel;
   int32_t part_blocks;
   int32_t max_parts;
-  size_t ws_o_bytes;
+  int64_t max_pairs;
+  size_t pairs_off;
+  size_t ws_o_off;
+  size_t ws_ml_off;
   size_t ws_bytes;
 };
 
@@ -65,7 +77,12 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   int32_t part = opts ? opts->partition_size : 0;
   if (part < 0) return PKV_ERR_SHAPE;
   if (part > 0 && part % align) return PKV_ERR_SHAPE;
-  if (part == 0) part = kernel == PKV_KERNEL_MFMA ? kAutoPartitionMfma : kAutoPartitionValu;
+  if (part == 0) {
+    const int64_t want = ((int64_t)max_context_len * num_seqs * num_kv_heads + kFillItems - 1) / kFillItems;
+    int64_t p2 = kMinAutoPartition;
+    while (p2 < want && p2 < max_context_len) p2 <<= 1;
+    part = (int32_t)(p2 < 0x40000000 ? p2 : 0x40000000);
+  }
   part = (int32_t)round_up(part, align);
 
   const int64_t ctx_blocks = ((int64_t)max_context_len + block_size - 1) / block_size;
@@ -78,14 +95,18 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   }
   if ((int64_t)num_seqs * num_kv_heads * plan->max_parts > kMaxGrid) return PKV_ERR_SHAPE;
   plan->kernel = kernel;
+  plan->max_pairs = (int64_t)num_seqs * plan->max_parts;
+  plan->pairs_off = round_up(sizeof(pkv::WorkHeader), 256);
+  plan->ws_o_off = plan->pairs_off + round_up((size_t)plan->max_pairs * sizeof(pkv::WorkPair), 256);
+  plan->ws_ml_off = plan->ws_o_off;
   if (plan->max_parts > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads * plan->max_parts;
-    plan->ws_o_bytes = round_up(rows * head_dim * sizeof(float), 256);
-    plan->ws_bytes = plan->ws_o_bytes + round_up(rows * 2 * sizeof(float), 256);
+    plan->ws_ml_off = plan->ws_o_off + round_up(rows * head_dim * sizeof(float), 256);
+    plan->ws_bytes = plan->ws_ml_off + round_up(rows * 2 * sizeof(float), 256);
   } else {
-    plan->ws_o_bytes = 0;
-    plan->ws_bytes = 0;
+    plan->ws_bytes = plan->ws_o_off;
   }
+  if (num_seqs == 0) plan->ws_bytes = 0;
   return PKV_OK;
 }
 
@@ -153,10 +174,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_ALIGN;
-  if (plan.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-  }
+  if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 
   pkv::AttnParams p;
   p.out = out;
@@ -165,10 +184,11 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
-  p.ws_o = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  p.ws_ml = plan.ws_bytes
-                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_o_bytes)
-                : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.work = reinterpret_cast<pkv::WorkHeader*>(ws);
+  p.pairs = reinterpret_cast<pkv::WorkPair*>(ws + plan.pairs_off);
+  p.ws_o = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_off) : nullptr;
+  p.ws_ml = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_ml_off) : nullptr;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
@@ -178,15 +198,17 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   p.num_blocks = num_blocks;
   p.part_blocks = plan.part_blocks;
   p.max_parts = plan.max_parts;
+  p.max_pairs = (int32_t)plan.max_pairs;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / num_kv_heads;
   clear_pending_error();
+  hipError_t err = pkv::launch_attention_plan(p, block_size, s);
+  if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_begin_event) {
     const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
     if (e != hipSuccess) return launch_status(e);
   }
-  hipError_t err = hipSuccess;
   const bool have = plan.kernel == PKV_KERNEL_MFMA
                         ? pkv::launch_attention_mfma(p, dtype, head_dim, block_size, group, s, &err)
                         : pkv::launch_attention_valu(p, dtype, head_dim, block_size, group, s, &err);

@@ -35,18 +35,23 @@ __device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
 // Safe reference point for 2^(x - m) when m may be -inf.
 __device__ __forceinline__ float softmax_ref(float m) { return m == -INFINITY ? 0.f : m; }
 
-// Linear workgroup index -> (sequence, kv head, partition); sequences vary
-// fastest, so workgroups that start together cover the same heads and
-// positions of neighbouring sequences.
-struct WorkItem { int s, h, part; };
+// Workgroup -> (sequence, kv head, partition) through the plan: pair
+// blockIdx / Hkv of the list, KV head blockIdx % Hkv.  The grid covers every
+// pair the list could hold; workgroups past its end (and entries that do not
+// name a sequence and partition of this call) do nothing.
+struct WorkItem { int s, h, part; bool valid; };
 
 __device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
-  int lin = blockIdx.x;
+  const int lin = blockIdx.x;
+  const int pair = lin / p.num_kv_heads;          // < max_pairs by the grid size
   WorkItem it;
-  it.s = lin % p.num_seqs;
-  lin /= p.num_seqs;
-  it.h = lin % p.num_kv_heads;
-  it.part = lin / p.num_kv_heads;
+  it.h = lin - pair * p.num_kv_heads;
+  const int n_pairs = min(p.work->n_pairs, p.max_pairs);
+  const WorkPair wp = p.pairs[pair];
+  it.s = wp.s;
+  it.part = wp.part;
+  it.valid = pair < n_pairs && (unsigned)wp.s < (unsigned)p.num_seqs &&
+             (unsigned)wp.part < (unsigned)p.max_parts;
   return it;
 }
 

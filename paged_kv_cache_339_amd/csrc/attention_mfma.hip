@@ -58,12 +58,13 @@ template <> struct Mfma<PKV_F16> {
 template <int DPL> struct VRow;
 template <> struct VRow<8> {
   typedef u32x4 type;
-  static __device__ __forceinline__ type load(const char* p) { return load16(p); }
+  static __device__ __forceinline__ type load(const char* p) { return load16_kv(p); }
   static __device__ __forceinline__ type zero() { return u32x4{0, 0, 0, 0}; }
 };
 template <> struct VRow<4> {
   typedef u32x2 type;
   static __device__ __forceinline__ type load(const char* p) {
+    if constexpr (PKV_NT_KV) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
     return *reinterpret_cast<const u32x2*>(p);
   }
   static __device__ __forceinline__ type zero() { return u32x2{0, 0}; }
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(AttnParams p) {
   __shared__ MergeSmem<D, G, NW> sm;
 
   const WorkItem it = work_item(p);
+  if (!it.valid) return;
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
     if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(AttnParams p) {
       }
       const char* kp = kbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tok % B) * D + 8 * q) * ES;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = ok ? load16(kp + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) kr[t][ks] = ok ? load16_kv(kp + 32 * ks * ES) : u32x4{0, 0, 0, 0};
     }
     // Values: tokens 8q .. 8q+7 (one block), elements DPL r .. DPL r + DPL.
     typename VR::type vr[8];

@@ -19,7 +19,7 @@
 
 namespace pkv {
 
-template <int DT, int D, int B, int G, int NW>
+template <int DT, int D, int B, int G, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   constexpr int ES = Format<DT>::kBytes;
   constexpr int EPL = 16 / ES;       // elements per lane per load
@@ -31,6 +31,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   __shared__ MergeSmem<D, G, NW> sm;
 
   const WorkItem it = work_item(p);
+  if (!it.valid) return;
+  const int lane = lane_id(), w = wave_id();
+  const int grp = lane / LPT, sub = lane % LPT;
+  const int Hkv = p.num_kv_heads;
+
+  // The first 64 table entries of the partition are fetched before the
+  // sequence length is known (they lie inside the row whatever the length),
+  // one per lane, so translating a block later is a register read.
+  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const int b0 = it.part * p.part_blocks;
+  int tab = -1;
+  if (lane < p.part_blocks && b0 + lane < p.max_blocks_per_seq) tab = table[b0 + lane];
+
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
     if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
@@ -41,10 +54,6 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
     return;
   }
   if (it.part >= sw.nparts) return;
-
-  const int lane = lane_id(), w = wave_id();
-  const int grp = lane / LPT, sub = lane % LPT;
-  const int Hkv = p.num_kv_heads;
 
   // Query rows of the G heads that share this KV head, pre-scaled.
   float qf[G][EPL];
@@ -66,93 +75,91 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const char* kbase = reinterpret_cast<const char*>(p.k_cache);
   const char* vbase = reinterpret_cast<const char*>(p.v_cache);
-  const int b0 = it.part * p.part_blocks;
   const int b1 = min(sw.nblk, b0 + p.part_blocks);
   const int tail = sw.L - (sw.nblk - 1) * B;      // tokens in the last block, 1..B
   int bad = 0;
 
-  for (int b = b0 + w; b < b1; b += NW) {
-    const int phys = table[b];
-    if ((unsigned)phys >= (unsigned)p.num_blocks) {
-      bad = 1;
-      continue;
-    }
-    const size_t lane_off = (((size_t)phys * Hkv + it.h) * B + grp) * D + sub * EPL;
-    const char* kt = kbase + lane_off * ES;
-    const char* vt = vbase + lane_off * ES;
-    const int valid = (b == sw.nblk - 1) ? tail : B;
-
-    u32x4 kr[NL], vr[NL];
-    if (valid == B) {
+  for (int c0 = b0; c0 < b1; c0 += kWave) {
+    if (c0 != b0) tab = (c0 + lane < b1) ? table[c0 + lane] : -1;
+    const int cn = min(kWave, b1 - c0);
+    // Wave w takes U consecutive blocks at a time; all their key and value
+    // loads are issued before any of them is used.
+    for (int j = w * U; j < cn; j += NW * U) {
+      u32x4 kr[U][NL], vr[U][NL];
+      int valid[U];
 #pragma unroll
-      for (int i = 0; i < NL; ++i) kr[i] = load16(kt + (size_t)i * TPW * D * ES);
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + u;
+        const bool in = jj < cn;
+        const int phys = __builtin_amdgcn_readlane(tab, in ? jj : 0);
+        const bool ok = in && (unsigned)phys < (unsigned)p.num_blocks;
+        bad |= in && !ok;
+        valid[u] = !ok ? 0 : (c0 + jj == sw.nblk - 1 ? tail : B);
+        const size_t lane_off = (((size_t)(ok ? phys : 0) * Hkv + it.h) * B + grp) * D + sub * EPL;
+        const char* kt = kbase + lane_off * ES;
+        const char* vt = vbase + lane_off * ES;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) vr[i] = load16(vt + (size_t)i * TPW * D * ES);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
-        if (i * TPW + grp < valid) {
-          kr[i] = load16(kt + (size_t)i * TPW * D * ES);
-          vr[i] = load16(vt + (size_t)i * TPW * D * ES);
+        for (int i = 0; i < NL; ++i) {
+          kr[u][i] = u32x4{0, 0, 0, 0};
+          vr[u][i] = u32x4{0, 0, 0, 0};
+          if (i * TPW + grp < valid[u]) {
+            kr[u][i] = load16_kv(kt + (size_t)i * TPW * D * ES);
+            vr[u][i] = load16_kv(vt + (size_t)i * TPW * D * ES);
+          }
         }
       }
-    }
 
-    float sc[G][NL];
+      float sc[G][U * NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float kf[EPL];
-      widen16<DT>(kr[i], kf);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          float kf[EPL];
+          widen16<DT>(kr[u][i], kf);
+          const bool row_ok = i * TPW + grp < valid[u];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) a = fmaf(qf[g][e], kf[e], a);
+            a = group_sum<LPT>(a);
+            sc[g][u * NL + i] = row_ok ? a : -INFINITY;
+          }
+        }
+
+      float pr[G][U * NL];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float a = 0.f;
+        float mx = sc[g][0];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) a = fmaf(qf[g][e], kf[e], a);
-        sc[g][i] = group_sum<LPT>(a);
-      }
-    }
-    if (valid != B) {
+        for (int i = 1; i < U * NL; ++i) mx = fmaxf(mx, sc[g][i]);
+        const float mn = fmaxf(m[g], mx);
+        const float ref = softmax_ref(mn);
+        const float alpha = fast_exp2(m[g] - ref);
+        float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < NL; ++i)
-        if (i * TPW + grp >= valid) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) sc[g][i] = -INFINITY;
+        for (int i = 0; i < U * NL; ++i) {
+          pr[g][i] = fast_exp2(sc[g][i] - ref);
+          ps += pr[g][i];
         }
-    }
-
-    float pr[G][NL];
+        l[g] = fmaf(l[g], alpha, ps);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = sc[g][0];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[g][i]);
-      const float mn = fmaxf(m[g], mx);
-      const float ref = softmax_ref(mn);
-      const float alpha = fast_exp2(m[g] - ref);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        pr[g][i] = fast_exp2(sc[g][i] - ref);
-        ps += pr[g][i];
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+        m[g] = mn;
       }
-      l[g] = fmaf(l[g], alpha, ps);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
-      m[g] = mn;
-    }
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float vf[EPL];
-      widen16<DT>(vr[i], vf);
+        for (int i = 0; i < NL; ++i) {
+          float vf[EPL];
+          widen16<DT>(vr[u][i], vf);
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+          for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[g][i], vf[e], acc[g][e]);
+            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pr[g][u * NL + i], vf[e], acc[g][e]);
+        }
     }
   }
 
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
       sm.m[w][g] = m[g];
       sm.l[w][g] = l[g];
     }
-    sm.bad[w] = bad;
+    sm.bad[w] = __any(bad);
   }
   __syncthreads();
   merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
@@ -196,13 +203,29 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kValuWaves = 4;
+#ifndef PKV_VALU_WAVES
+#define PKV_VALU_WAVES 4
+#endif
+#ifndef PKV_VALU_UNROLL
+#define PKV_VALU_UNROLL 2
+#endif
+#ifndef PKV_VALU_LDS_PAD
+#define PKV_VALU_LDS_PAD 0
+#endif
+constexpr int kValuWaves = PKV_VALU_WAVES;
+
+// Blocks a wave loads ahead: two tiles of 8 fp32 rows of 128 already make
+// 64 KiB of registers per wave in flight, so f32 and wide groups take one.
+template <int DT, int D, int G>
+constexpr int valu_unroll() {
+  return (DT == PKV_F32 && D == 128) || G >= 4 ? 1 : PKV_VALU_UNROLL;
+}
 
 template <int DT, int D, int B, int G>
 hipError_t launch_valu(const AttnParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
-  hipLaunchKernelGGL((attn_valu_kernel<DT, D, B, G, kValuWaves>), grid, dim3(kValuWaves * kWave), 0,
-                     st, p);
+  hipLaunchKernelGGL((attn_valu_kernel<DT, D, B, G, kValuWaves, valu_unroll<DT, D, G>()>), grid,
+                     dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
   return hipGetLastError();
 }
 

@@ -8,6 +8,18 @@
 
 namespace pkv {
 
+// Work list of one decode call, written by the plan kernel into the head of
+// the workspace and read by the attention kernels: (sequence, partition)
+// pairs, longest work first.
+struct WorkHeader {
+  int32_t n_pairs;
+  int32_t pad[63];
+};
+struct WorkPair {
+  int32_t s;
+  int32_t part;
+};
+
 // Everything the decode-attention kernels read.  Sizes are validated by the
 // C ABI before a launch.
 struct AttnParams {
@@ -19,6 +31,8 @@ struct AttnParams {
   const int32_t* context_lens;  // [S]
   float* ws_o;                // [S, Hq, P, D] partition outputs, normalised
   float* ws_ml;               // [S, Hq, P, 2]  (running max in log2 units, sum)
+  WorkHeader* work;           // plan written by the plan kernel
+  WorkPair* pairs;            // [max_pairs]
   float scale_log2;           // scale * log2(e)
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -28,6 +42,7 @@ struct AttnParams {
   int32_t num_blocks;
   int32_t part_blocks;        // blocks per split-K partition
   int32_t max_parts;          // partitions per sequence covered by the grid
+  int32_t max_pairs;          // num_seqs * max_parts, the room of `pairs`
 };
 
 // Returns false when no kernel instance exists for the combination.
@@ -35,6 +50,7 @@ bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int 
                            int group, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                            int group, hipStream_t stream, hipError_t* err);
+hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
 bool launch_attention_reduce(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                              hipStream_t stream, hipError_t* err);
 

@@ -73,7 +73,8 @@ CONFIGS = {
                     len_lo=1024, len_hi=32768, partition_size=512),
     5: DecodeConfig("shared_prefix_sampling_bf16", num_seqs=512, num_q_heads=40, num_kv_heads=40,
                     head_dim=128, dtype="bf16", block_size=16, lengths="shared_prefix",
-                    len_lo=1, len_hi=512, prompt_len=1000, samples_per_prompt=8),
+                    len_lo=1, len_hi=512, prompt_len=1000, samples_per_prompt=8,
+                    partition_size=1024),
 }
 
 

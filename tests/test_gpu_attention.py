@@ -166,3 +166,52 @@ def test_gqa_matches_replicated_mha_within_tolerance():
     Vr = [np.repeat(v, Hq // Hkv, axis=1) for v in V]
     m = _paged_on_gpu(pins.Paged(Kr, Vr, q, 32, "bf16", 6), "bf16", 0.088, Hq, "valu")
     assert_rows_close(widen(g), widen(m), "bf16", "GQA vs MHA")
+
+
+def test_work_list_covers_every_partition_longest_first():
+    """The plan at the head of the workspace (after a 256-byte header whose
+    first int32 is the pair count) names every (sequence, partition) pair of
+    the call exactly once: full partitions in sequence order, then the
+    shorter last partitions by non-increasing size, then empty sequences."""
+    rng = np.random.default_rng(17)
+    B, part = 16, 512
+    lens = rng.integers(1, 3000, size=37)
+    lens[[3, 20]] = 0
+    lens[7] = 512
+    lens[9] = 1024
+    cfg = _edge_cfg("bf16", 128, B, 4, 2).scaled(num_seqs=len(lens))
+    lay = make_layout(cfg, 21, lengths=lens)
+    step = DeviceStep.from_host(lay, host_values(lay))
+    max_ctx = int(lens.max())
+    need = pkv.workspace_bytes(len(lens), 4, 2, 128, B, max_ctx, 2, partition_size=part)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(step.q)
+    say("work list order")
+    pkv.paged_attention_decode(out, step.q, step.k_cache, step.v_cache, step.tables, step.lens, cfg.scale, B, 2,
+                               max_ctx, partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    n = int(raw[:4].view(np.int32)[0])
+    pairs = raw[256:].view(np.int32)[: 2 * n].reshape(-1, 2)
+    pb = part // B
+    want, full = set(), []
+    for s, L in enumerate(lens.tolist()):
+        nblk = -(-L // B)
+        if L == 0:
+            want.add((s, 0))
+        for k in range(-(-nblk // pb)):
+            want.add((s, k))
+            if nblk - k * pb >= pb:
+                full.append((s, k))
+    got = [tuple(x) for x in pairs.tolist()]
+    assert len(got) == len(want) and set(got) == want, "work list is not the set of partitions"
+    assert got[:len(full)] == full, "full partitions must come first, in sequence order"
+
+    def size(sp):
+        s, k = sp
+        nblk = -(-int(lens[s]) // B)
+        return min(pb, nblk - k * pb)
+
+    rest = [size(x) for x in got[len(full):]]
+    assert all(a >= b for a, b in zip(rest, rest[1:])), "last partitions must come longest first"
+    assert rest[-2:] == [0, 0], "empty sequences come last"

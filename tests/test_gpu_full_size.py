@@ -1,0 +1,66 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (its seeds, its device-drawn values, its partition sizes),
+on sampled sequences: their blocks, tables and inputs are copied to the host
+before any library kernel runs, the library then runs the whole step on the
+full batch, and the oracle recomputes the sampled rows one sequence at a
+time.  The scatter is checked bit-exactly at every slot of the batch; the
+copy-on-write copies of the shared-prefix workload bit-exactly too."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_339_amd as pkv
+from synthetic import CONFIGS, device_values, make_layout
+from tests.gpu_util import (DeviceStep, assert_rows_close, ints, oracle_on_snapshot, say,
+                            snapshot_sequences, widen)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(lay, k, rng):
+    lens = lay.context_lens
+    picks = {int(np.argmax(lens)), int(np.argmin(lens))}
+    while len(picks) < min(k, len(lens)):
+        picks.add(int(rng.integers(len(lens))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_sampled_rows(idx):
+    cfg = CONFIGS[idx]
+    lay = make_layout(cfg, seed=idx)
+    say(f"full-size config {idx} ({cfg.name}): S={len(lay.context_lens)} pool={lay.num_blocks} blocks")
+    step = DeviceStep.from_device_values(lay, device_values(lay, device="cuda"))
+    rng = np.random.default_rng(100 + idx)
+    seqs = _sample(lay, 6 if idx == 4 else 10, rng)
+    snap = snapshot_sequences(step, seqs)
+    torch.cuda.synchronize()
+
+    if len(lay.cow_pairs):
+        # The copies a diverging sample makes, into blocks the tables leave free.
+        spare = lay.pool_order[lay.used_blocks:lay.used_blocks + len(lay.cow_pairs)]
+        pairs = np.stack([lay.cow_pairs[:, 0], spare], axis=1).astype(np.int32)
+        pkv.copy_blocks(step.k_cache, step.v_cache, ints(pairs))
+        torch.cuda.synchronize()
+        sel = rng.choice(len(pairs), size=16, replace=False)
+        src = torch.from_numpy(pairs[sel, 0].astype(np.int64)).cuda()
+        dst = torch.from_numpy(pairs[sel, 1].astype(np.int64)).cuda()
+        for cache in (step.k_cache, step.v_cache):
+            assert torch.equal(cache[src].view(torch.int16), cache[dst].view(torch.int16)), "copy_blocks"
+
+    step.scatter()
+    out = step.attend(partition_size=cfg.partition_size)
+    torch.cuda.synchronize()
+
+    # Every appended token sits at its slot, bit for bit.
+    B = cfg.block_size
+    slots = torch.from_numpy(lay.new_slots.astype(np.int64)).cuda()
+    for cache, new in ((step.k_cache, step.k_new), (step.v_cache, step.v_new)):
+        rows = cache[slots // B, :, slots % B, :]
+        assert torch.equal(rows.contiguous().view(torch.int16), new.view(torch.int16)), "reshape_and_cache"
+
+    want = oracle_on_snapshot(snap, cfg)
+    got = widen(out.index_select(0, torch.tensor(seqs, device="cuda")))
+    err = assert_rows_close(got, want, cfg.dtype, f"config {idx} full size")
+    say(f"config {idx}: sampled sequences {seqs}, max row-relative error {err:.2e}")
