@@ -55,7 +55,7 @@ enum pkv_status {
   PKV_ERR_DTYPE = -3,       /* unknown dtype */
   PKV_ERR_UNSUPPORTED = -4, /* a valid combination this build has no kernel for */
   PKV_ERR_ALIGN = -5,       /* a data pointer is not 16-byte aligned */
-  PKV_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small */
+  PKV_ERR_WORKSPACE = -6,   /* workspace missing or too small */
   PKV_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch */
   PKV_ERR_NO_BLOCKS = -8,   /* block manager: the free list is empty */
   PKV_ERR_STATE = -9,       /* block manager: unknown/duplicate sequence, bad block */
@@ -80,22 +80,30 @@ enum pkv_kernel {
 };
 
 typedef struct pkv_attn_options {
-  /* Tokens per split-K partition.  0 = automatic; otherwise a positive
-   * multiple of block_size (and of 32 for the MFMA kernel).  A sequence of
-   * length L is cut into ceil(L / partition_size) partitions that are
-   * processed by separate workgroups and merged by a reduce kernel. */
+  /* Tokens per split-K partition.  0 = automatic: the smallest power of two
+   * of at least 1024 tokens that leaves about 2560 (sequence, KV head,
+   * partition) work items if every sequence were max_context_len long (one
+   * partition when that already covers max_context_len).  Otherwise a
+   * positive multiple of block_size (and of 32 for the MFMA kernel).  A
+   * sequence of length L is cut into ceil(L / partition_size) partitions
+   * that separate workgroups process; a reduce kernel merges them. */
   int32_t partition_size;
   int32_t kernel;            /* enum pkv_kernel */
   /* Optional hipEvent_t handles (NULL = none), recorded on the stream right
    * before and right after the main attention kernel, so a caller can time
-   * that kernel alone.  The reduce kernel, if any, runs after main_end. */
+   * that kernel alone.  The plan kernel runs before main_begin, the reduce
+   * kernel (if any) after main_end.  Recording an event between two kernels
+   * delays the second one by a few microseconds. */
   void* main_begin_event;
   void* main_end_event;
 } pkv_attn_options;
 
-/* Bytes of split-K workspace pkv_paged_attention_decode needs for these
- * sizes and options (0 when no sequence can span two partitions).  Returns
- * 0 on invalid arguments as well; the decode call reports those. */
+/* Bytes of workspace pkv_paged_attention_decode needs for these sizes and
+ * options: a 256-byte header and the work list (8 bytes per sequence and
+ * partition), plus fp32 partition results (head_dim + 2 floats per
+ * sequence, query head and partition) when a sequence can span several
+ * partitions.  0 for an empty batch, and 0 on invalid arguments (the decode
+ * call reports those). */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
                                            int32_t block_size, int32_t max_context_len,
@@ -120,12 +128,21 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * Device pointers: out, q, k_cache, v_cache (16-byte aligned), block_tables,
  * context_lens, workspace.  max_context_len (host) must be >= every
  * context_lens[s]; it sizes the launch.  num_blocks is the pool size.
+ *
+ * Launches, in stream order: a one-workgroup plan kernel that reads
+ * context_lens and writes the work list into the workspace (the
+ * (sequence, partition) pairs, longest first, so long pieces start early
+ * and the grid ends on short ones); the main kernel, one workgroup per
+ * (pair, KV head); and, when max_context_len exceeds the partition, the
+ * split-K reduce.  The schedule does not change any result.
  * Data errors are contained, never dereferenced: a table entry outside
  * [0, num_blocks), or context_lens[s] above max_context_len or
  * max_blocks_per_seq * B, makes that sequence's output rows NaN.
  * head_dim: 64 or 128.  block_size: 8, 16, 32 or 64.
- * workspace: device memory of at least pkv_paged_attention_workspace_bytes
- * (may be NULL when that is 0); its contents need no initialisation.
+ * workspace: device memory of at least pkv_paged_attention_workspace_bytes,
+ * 16-byte aligned, required whenever num_seqs > 0; its contents need no
+ * initialisation and are overwritten.  Calls that overlap in time must not
+ * share a workspace.
  * opts may be NULL (automatic everything).
  */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

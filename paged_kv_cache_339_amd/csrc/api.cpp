@@ -136,7 +136,7 @@ const char* pkv_status_str(int status) {
     case PKV_ERR_DTYPE: return "unknown dtype";
     case PKV_ERR_UNSUPPORTED: return "no kernel for this combination";
     case PKV_ERR_ALIGN: return "data pointer not 16-byte aligned";
-    case PKV_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_NO_BLOCKS: return "block pool exhausted";
     case PKV_ERR_STATE: return "invalid block manager state or sequence";
