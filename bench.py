@@ -69,6 +69,15 @@ def _oracle_rows(s):
     return s
 
 
+def _one_blas_thread():
+    """Each worker process runs single-threaded BLAS (one worker per core)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
 def cpu_baseline(cfg, layout, cpu_seconds: float):
     import multiprocessing as mp
 
@@ -91,14 +100,15 @@ def cpu_baseline(cfg, layout, cpu_seconds: float):
     _CPU.update(cfg=cfg, q=host.q, k=host.k_cache, v=host.v_cache, tables=sub.block_tables,
                 lens=sub.context_lens)
     ctx = mp.get_context("fork")
-    with ctx.Pool(workers) as pool:
-        t0 = time.perf_counter()
-        pool.map(_oracle_rows, range(k), chunksize=1)
-        one = time.perf_counter() - t0
-        reps = int(min(100000, max(1, math.ceil(cpu_seconds / max(one, 1e-3)))))
-        t0 = time.perf_counter()
-        pool.map(_oracle_rows, list(range(k)) * reps, chunksize=1)
-        elapsed = time.perf_counter() - t0
+    with ctx.Pool(workers, initializer=_one_blas_thread) as pool:
+        pool.map(_oracle_rows, range(k), chunksize=1)          # warm the workers
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            pool.map(_oracle_rows, range(k), chunksize=1)
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= cpu_seconds:
+                break
     nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.dtype) * reps
     return {
         "value": round(nbytes / elapsed / 1e9, 4),

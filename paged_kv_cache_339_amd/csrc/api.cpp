@@ -235,11 +235,11 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
     return PKV_ERR_SHAPE;
   if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_heads * head_dim * es / 16 > 0x7fffffff / 16) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_ALIGN;
-  if ((int64_t)num_tokens * num_kv_heads * head_dim * es / 16 / 256 >= kMaxGrid) return PKV_ERR_SHAPE;
   clear_pending_error();
   return launch_status(pkv::launch_reshape_and_cache(
       k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim * es, block_size,

@@ -14,31 +14,28 @@
 
 namespace pkv {
 
-constexpr int kPlanThreads = 256;
-constexpr int kPlanWaves = kPlanThreads / kWave;
-constexpr int kPlanBins = kPlanThreads;
+// One wave does the whole plan: the work is a few hundred sequences, and a
+// single wave needs no workgroup barriers.  Sequences s = lane + 64 k are
+// held by lane `lane`; up to kPlanCached of them per lane stay in registers
+// between the two passes, longer batches re-read context_lens.
+constexpr int kPlanBins = 256;
+constexpr int kPlanCached = 8;
 
-// Exclusive prefix sum over the workgroup: a scan within each wave by lane
-// shuffles, then the wave totals through LDS.  *total receives the sum.
-__device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
-  const int lane = lane_id(), w = wave_id();
-  int incl = v;
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const int x = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += x;
+    const int x = __shfl_up(v, off, kWave);
+    if (lane >= off) v += x;
   }
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  int before = 0, sum = 0;
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
-  for (int i = 0; i < kPlanWaves; ++i) {
-    before += i < w ? wave_tot[i] : 0;
-    sum += wave_tot[i];
-  }
-  __syncthreads();
-  *total = sum;
-  return before + incl - v;
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
 }
 
 // Bin of a last partition of r blocks (1 <= r < P): larger r, larger bin;
@@ -47,73 +44,110 @@ __device__ __forceinline__ int size_bin(int r, int P) {
   return 1 + (int)((int64_t)(r - 1) * (kPlanBins - 1) / P);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnParams p, int B) {
+// What one sequence contributes: `nfull` full partitions, and one item in
+// bin `bin` (a shorter last partition, or bin 0 for no work), or none (-1).
+struct SeqPlan { int nfull, bin; };
+
+__device__ __forceinline__ SeqPlan seq_plan(const AttnParams& p, int s, int B) {
+  const SeqWork w = seq_work(p, s, B);
+  SeqPlan sp;
+  if (w.bad || w.L == 0) {
+    sp.nfull = 0;
+    sp.bin = 0;
+  } else {
+    sp.nfull = w.nblk / p.part_blocks;
+    const int r = w.nblk % p.part_blocks;
+    sp.bin = r ? size_bin(r, p.part_blocks) : -1;
+  }
+  return sp;
+}
+
+// Pass-2 step for one chunk of 64 sequences: full partitions at the running
+// prefix `carry` (sequence order), the other item at the next slot of its bin.
+__device__ __forceinline__ void write_pairs(const AttnParams& p, int s, SeqPlan sp, int* carry,
+                                            int* bins) {
+  const int incl = wave_inclusive_scan(sp.nfull);
+  const int first = *carry + incl - sp.nfull;
+  *carry += __shfl(incl, kWave - 1, kWave);
+  for (int k = 0; k < sp.nfull && first + k < p.max_pairs; ++k) p.pairs[first + k] = WorkPair{s, k};
+  if (sp.bin >= 0) {
+    const int pos = atomicAdd(&bins[sp.bin], 1);
+    if (pos < p.max_pairs) p.pairs[pos] = WorkPair{s, sp.nfull};
+  }
+}
+
+__global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) {
   __shared__ int bins[kPlanBins];
-  __shared__ int wave_tot[kPlanWaves];
-  __shared__ int full_total;
-  const int t = threadIdx.x;
-  const int P = p.part_blocks;
-  bins[t] = 0;
-  if (t == 0) full_total = 0;
+  const int lane = lane_id();
+  const int S = p.num_seqs;
+  const int chunks = (S + kWave - 1) / kWave;
+#pragma unroll
+  for (int i = 0; i < kPlanBins / kWave; ++i) bins[lane + i * kWave] = 0;
   __syncthreads();
 
   // Pass 1: count full partitions, histogram the rest.
-  for (int s = t; s < p.num_seqs; s += kPlanThreads) {
-    const SeqWork w = seq_work(p, s, B);
-    if (w.bad || w.L == 0) {
-      atomicAdd(&bins[0], 1);
-    } else {
-      atomicAdd(&full_total, w.nblk / P);
-      const int r = w.nblk % P;
-      if (r) atomicAdd(&bins[size_bin(r, P)], 1);
-    }
+  SeqPlan cached[kPlanCached];
+  int full_total = 0;
+#pragma unroll
+  for (int c = 0; c < kPlanCached; ++c) {
+    const int s = c * kWave + lane;
+    cached[c] = SeqPlan{0, -1};
+    if (s < S) cached[c] = seq_plan(p, s, B);
   }
+#pragma unroll
+  for (int c = 0; c < kPlanCached; ++c) {
+    full_total += cached[c].nfull;
+    if (cached[c].bin >= 0) atomicAdd(&bins[cached[c].bin], 1);
+  }
+  for (int c = kPlanCached; c < chunks; ++c) {
+    const int s = c * kWave + lane;
+    SeqPlan sp{0, -1};
+    if (s < S) sp = seq_plan(p, s, B);
+    full_total += sp.nfull;
+    if (sp.bin >= 0) atomicAdd(&bins[sp.bin], 1);
+  }
+  full_total = wave_sum(full_total);
   __syncthreads();
 
   // Start of each bin: full partitions first, then bins from the largest
-  // size down, bin 0 last (thread t takes bin kPlanBins-1-t, the last thread
-  // bin 0).
+  // size down, bin 0 last.  Lane l owns the four bins 255-4l .. 252-4l.
   {
-    const int bin = t < kPlanBins - 1 ? kPlanBins - 1 - t : 0;
-    int total;
-    const int start = block_exclusive_scan(bins[bin], wave_tot, &total);
-    const int nfull = full_total;
+    int cnt[kPlanBins / kWave], local = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanBins / kWave; ++i) {
+      cnt[i] = bins[kPlanBins - 1 - (lane * (kPlanBins / kWave) + i)];
+      local += cnt[i];
+    }
+    const int incl = wave_inclusive_scan(local);
+    int start = full_total + incl - local;
     __syncthreads();
-    bins[bin] = nfull + start;
-    if (t == 0) p.work->n_pairs = min(nfull + total, p.max_pairs);
+#pragma unroll
+    for (int i = 0; i < kPlanBins / kWave; ++i) {
+      const int b = kPlanBins - 1 - (lane * (kPlanBins / kWave) + i);
+      // bin 0 goes after every other bin: the scan order puts it last already.
+      bins[b] = start;
+      start += cnt[i];
+    }
+    if (lane == kWave - 1) p.work->n_pairs = min(full_total + incl, p.max_pairs);
     __syncthreads();
   }
 
-  // Pass 2: write the pairs.  Full partitions keep sequence order (prefix sum
-  // of their counts, chunk by chunk); the others take the next slot of their bin.
+  // Pass 2: full partitions in sequence order, the rest into their bins.
   int carry = 0;
-  for (int base = 0; base < p.num_seqs; base += kPlanThreads) {
-    const int s = base + t;
-    SeqWork w;
-    int nfull = 0;
-    if (s < p.num_seqs) {
-      w = seq_work(p, s, B);
-      if (!w.bad && w.L > 0) nfull = w.nblk / P;
-    }
-    int chunk_total;
-    const int first = carry + block_exclusive_scan(nfull, wave_tot, &chunk_total);
-    carry += chunk_total;
-    if (s < p.num_seqs) {
-      for (int k = 0; k < nfull && first + k < p.max_pairs; ++k) p.pairs[first + k] = WorkPair{s, k};
-      int pos = -1, part = 0;
-      if (w.bad || w.L == 0) {
-        pos = atomicAdd(&bins[0], 1);
-      } else if (w.nblk % P) {
-        pos = atomicAdd(&bins[size_bin(w.nblk % P, P)], 1);
-        part = nfull;
-      }
-      if (pos >= 0 && pos < p.max_pairs) p.pairs[pos] = WorkPair{s, part};
-    }
+#pragma unroll
+  for (int c = 0; c < kPlanCached; ++c) {
+    if (c < chunks) write_pairs(p, c * kWave + lane, cached[c], &carry, bins);
+  }
+  for (int c = kPlanCached; c < chunks; ++c) {
+    const int s = c * kWave + lane;
+    SeqPlan sp{0, -1};
+    if (s < S) sp = seq_plan(p, s, B);
+    write_pairs(p, s, sp, &carry, bins);
   }
 }
 
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, block_size);
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kWave), 0, stream, p, block_size);
   return hipGetLastError();
 }
 

@@ -7,24 +7,29 @@
 
 namespace pkv {
 
-// One thread per 16-byte chunk of a (token, head) row.
+// One workgroup per new token: its slot is read once (a scalar load issued
+// together with the first key/value loads, which do not depend on it), then
+// the token's Hkv rows are moved 16 bytes per thread.  32-bit index math.
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
-    char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int64_t total,
-    int32_t num_kv_heads, int32_t chunks, int32_t block_size, int64_t num_slots) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = (int)(idx % chunks);
-  const int64_t row = idx / chunks;           // token * Hkv + head
-  const int h = (int)(row % num_kv_heads);
-  const int64_t i = row / num_kv_heads;
+    char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
+    int32_t chunks, int32_t block_size, int64_t num_slots) {
+  const int i = blockIdx.x;
   const int32_t slot = slot_mapping[i];
-  if (slot < 0 || (int64_t)slot >= num_slots) return;
-  const int64_t blk = slot / block_size, off = slot % block_size;
-  const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
-  const size_t src = ((size_t)row * chunks + c) * 16;
-  store16(k_cache + dst, load16(k + src));
-  store16(v_cache + dst, load16(v + src));
+  const int per_tok = num_kv_heads * chunks;        // 16-byte pieces of one token
+  const char* ks = k + (size_t)i * per_tok * 16;
+  const char* vs = v + (size_t)i * per_tok * 16;
+  const bool ok = slot >= 0 && (int64_t)slot < num_slots;
+  const int blk = ok ? slot / block_size : 0, off = ok ? slot % block_size : 0;
+  for (int j = threadIdx.x; j < per_tok; j += blockDim.x) {
+    const u32x4 a = load16(ks + (size_t)j * 16);
+    const u32x4 b = load16(vs + (size_t)j * 16);
+    if (!ok) continue;
+    const int h = j / chunks, c = j - h * chunks;
+    const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
+    store16(k_cache + dst, a);
+    store16(v_cache + dst, b);
+  }
 }
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -32,12 +37,12 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
                                     int32_t num_blocks, hipStream_t stream) {
   const int32_t chunks = row_bytes / 16;
-  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
-  if (total == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  hipLaunchKernelGGL(reshape_and_cache_kernel, grid, dim3(256), 0, stream,
+  if (num_tokens == 0) return hipSuccess;
+  const int per_tok = num_kv_heads * chunks;
+  const int threads = per_tok >= 256 ? 256 : (per_tok + 63) / 64 * 64;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)num_tokens), dim3(threads), 0, stream,
                      static_cast<const char*>(k), static_cast<const char*>(v),
-                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), slot_mapping, total,
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), slot_mapping,
                      num_kv_heads, chunks, block_size, (int64_t)num_blocks * block_size);
   return hipGetLastError();
 }
