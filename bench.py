@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of one paged-attention decode step on one MI355X.
 
-A step is the whole decode hot path for one batch: reshape_and_cache of the
-token each sequence appends (plus copy_blocks when the workload has
-copy-on-write pairs), then paged decode attention over all cached tokens
-(main kernel + split-K reduce).  Inputs are synthetic, seeded, N(0, 1), and
+A step is the whole decode hot path for one batch: copy_blocks when the
+workload has copy-on-write pairs, then pkv_decode_step, which stores the
+token each sequence appends (reshape_and_cache) in the launch that builds
+the attention work list, and runs paged decode attention over all cached
+tokens (main kernel, plus the split-K reduce when partitions split a
+sequence).  Inputs are synthetic, seeded, N(0, 1), and
 resident in HBM before timing starts.  The default workload is a
 Llama-2-7B-shaped layer: batch 64, 32 heads, head_dim 128, fp16 KV cache in
 16-token blocks, context lengths uniform in [128, 2048], blocks scattered at
@@ -295,34 +297,31 @@ def main():
 
     ev = HipEvents()
     vp = ctypes.c_void_p
-    scatter_args = (vp(kn.data_ptr()), vp(vn.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
-                    vp(slots.data_ptr()), S, Hkv, D, B, layout.num_blocks, code, vp(stream))
     copy_args = None
     if pairs is not None:
         copy_args = (vp(kc.data_ptr()), vp(vc.data_ptr()), vp(pairs.data_ptr()), n_pairs, Hkv, B, D,
                      layout.num_blocks, code, vp(stream))
 
-    def attn_args(opts):
-        return (vp(out.data_ptr()), vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
-                vp(tables.data_ptr()), vp(lens.data_ptr()), cfg.scale, B, Hkv, S, Hq, D,
-                layout.block_tables.shape[1], max_ctx, layout.num_blocks, code, vp(ws.data_ptr()),
-                ws.numel(), ctypes.byref(opts), vp(stream))
+    def step_args(opts):
+        """pkv_decode_step: store each sequence's new token and attend."""
+        return (vp(out.data_ptr()), vp(q.data_ptr()), vp(kn.data_ptr()), vp(vn.data_ptr()), vp(kc.data_ptr()),
+                vp(vc.data_ptr()), vp(slots.data_ptr()), vp(tables.data_ptr()), vp(lens.data_ptr()), cfg.scale,
+                B, Hkv, S, Hq, D, layout.block_tables.shape[1], max_ctx, layout.num_blocks, code,
+                vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream))
 
     K, W = args.steps, args.warmup
     begins = [ev.create() for _ in range(K)]
     ends = [ev.create() for _ in range(K)]
     plain = AttnOptions(part, KERNELS[args.kernel], None, None)
     timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i]) for i in range(K)]
-    warm_args = attn_args(plain)
-    timed_args = [attn_args(o) for o in timed]
+    warm_args = step_args(plain)
+    timed_args = [step_args(o) for o in timed]
 
     def step(a):
         if copy_args is not None:
             st = lib.pkv_copy_blocks(*copy_args)
             assert st == 0, st
-        st = lib.pkv_reshape_and_cache(*scatter_args)
-        assert st == 0, st
-        st = lib.pkv_paged_attention_decode(*a)
+        st = lib.pkv_decode_step(*a)
         assert st == 0, st
 
     for _ in range(W):
@@ -377,7 +376,7 @@ def main():
             "kv_dtype": cfg.dtype, "context_lens": LENGTH_DESC[args.config],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
             "kv_bytes_per_step": step_kv, "partition_size": part, "kernel": kernel_used,
-            "step": ("copy_blocks + " if copy_args else "") + "reshape_and_cache + paged_attention_decode",
+            "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
         },
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "seq_heads_per_s": round(S * Hq / step_s, 1),

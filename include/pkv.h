@@ -154,6 +154,24 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                void* workspace, size_t workspace_bytes,
                                const pkv_attn_options* opts, void* stream);
 
+/*
+ * One decode step in two launches: every sequence's new token is stored as
+ * pkv_reshape_and_cache would (token i = sequence i, slot slot_mapping[i])
+ * by the same launch that builds the attention work list, then attention
+ * runs as pkv_paged_attention_decode over context_lens (which count the new
+ * token).  Results are bit-identical to those two calls in sequence; the
+ * step saves one launch.  k_new, v_new: device [num_seqs, num_kv_heads,
+ * head_dim], 16-byte aligned; slot_mapping: device int32 [num_seqs].  Other
+ * arguments, workspace and errors as pkv_paged_attention_decode.
+ */
+int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
+                    const int32_t* context_lens, float scale, int32_t block_size,
+                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
+                    pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                    const pkv_attn_options* opts, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Cache write and copy-on-write                                             */
 /* ------------------------------------------------------------------------ */

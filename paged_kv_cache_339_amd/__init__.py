@@ -16,6 +16,7 @@ from ._lib import LIB_PATH, PkvError, check, lib
 from .ops import (
     BlockManager,
     copy_blocks,
+    decode_step,
     gather_kv,
     paged_attention_decode,
     reshape_and_cache,
@@ -23,6 +24,6 @@ from .ops import (
 )
 
 __all__ = [
-    "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "gather_kv",
+    "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
     "paged_attention_decode", "reshape_and_cache", "workspace_bytes",
 ]

@@ -47,6 +47,8 @@ def load(path: str = LIB_PATH):
         "pkv_paged_attention_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32,
                                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                                       c_vp, c_size, ctypes.POINTER(AttnOptions), c_vp]),
+        "pkv_decode_step": (ctypes.c_int, [c_vp] * 9 + [c_f32] + [c_i32] * 8 + [ctypes.c_int, c_vp, c_size,
+                                                                              ctypes.POINTER(AttnOptions), c_vp]),
         "pkv_reshape_and_cache": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                                  c_i32, ctypes.c_int, c_vp]),
         "pkv_copy_blocks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,

@@ -156,14 +156,18 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
   return plan.ws_bytes;
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               float scale, int32_t block_size, int32_t num_kv_heads,
-                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                               int32_t max_blocks_per_seq, int32_t max_context_len,
-                               int32_t num_blocks, pkv_dtype dtype, void* workspace,
-                               size_t workspace_bytes, const pkv_attn_options* opts,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode attention; with `append`, the launch that builds the work list also
+// stores every sequence's new token (a decode step in two launches).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                int32_t num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append) {
   Plan plan;
   const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, dtype, opts, &plan);
@@ -203,7 +207,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / num_kv_heads;
   clear_pending_error();
-  hipError_t err = pkv::launch_attention_plan(p, block_size, s);
+  hipError_t err = append ? pkv::launch_append_and_plan(p, block_size, *append, s)
+                          : pkv::launch_attention_plan(p, block_size, s);
   if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_begin_event) {
     const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
@@ -224,6 +229,50 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
     if (err != hipSuccess) return launch_status(err);
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, int32_t block_size, int32_t num_kv_heads,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t num_blocks, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, const pkv_attn_options* opts,
+                               void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                     max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts, stream,
+                     nullptr);
+}
+
+int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
+                    const int32_t* context_lens, float scale, int32_t block_size,
+                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
+                    pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                    const pkv_attn_options* opts, void* stream) {
+  const int es = dtype_bytes(dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (num_seqs > 0) {
+    if (!k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ALIGN;
+  }
+  pkv::AppendArgs a;
+  a.k = static_cast<const char*>(k_new);
+  a.v = static_cast<const char*>(v_new);
+  a.k_cache = static_cast<char*>(k_cache);
+  a.v_cache = static_cast<char*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.chunks = head_dim * es / 16;
+  a.num_slots = (int64_t)num_blocks * block_size;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                     num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                     max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts, stream, &a);
 }
 
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -11,6 +11,7 @@
 // slots past the end of the list do nothing and come last.
 // The order only schedules work: each pair's result does not depend on it.
 #include "attention_common.h"
+#include "scatter.h"
 
 namespace pkv {
 
@@ -76,7 +77,7 @@ __device__ __forceinline__ void write_pairs(const AttnParams& p, int s, SeqPlan 
   }
 }
 
-__global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) {
+__device__ __forceinline__ void plan_body(const AttnParams& p, int B) {
   __shared__ int bins[kPlanBins];
   const int lane = lane_id();
   const int S = p.num_seqs;
@@ -144,6 +145,27 @@ __global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) {
     if (s < S) sp = seq_plan(p, s, B);
     write_pairs(p, s, sp, &carry, bins);
   }
+}
+
+__global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) { plan_body(p, B); }
+
+// A decode step's first launch: workgroup 0 builds the work list, workgroup
+// 1 + i stores sequence i's new token.  Neither reads what the other writes
+// (the plan reads only context_lens), so they share one launch.
+__global__ __launch_bounds__(kWave) void append_and_plan_kernel(AttnParams p, int B, AppendArgs a) {
+  if (blockIdx.x == 0) {
+    plan_body(p, B);
+    return;
+  }
+  scatter_token(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, blockIdx.x - 1, p.num_kv_heads,
+                a.chunks, B, a.num_slots);
+}
+
+hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(append_and_plan_kernel, dim3((unsigned)p.num_seqs + 1), dim3(kWave), 0, stream,
+                     p, block_size, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream) {

@@ -4,32 +4,17 @@
 // move 16-byte units with vector loads and stores; none looks at values.
 #include "device_common.h"
 #include "kernels.h"
+#include "scatter.h"
 
 namespace pkv {
 
-// One workgroup per new token: its slot is read once (a scalar load issued
-// together with the first key/value loads, which do not depend on it), then
-// the token's Hkv rows are moved 16 bytes per thread.  32-bit index math.
+// One workgroup per new token.
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
     int32_t chunks, int32_t block_size, int64_t num_slots) {
-  const int i = blockIdx.x;
-  const int32_t slot = slot_mapping[i];
-  const int per_tok = num_kv_heads * chunks;        // 16-byte pieces of one token
-  const char* ks = k + (size_t)i * per_tok * 16;
-  const char* vs = v + (size_t)i * per_tok * 16;
-  const bool ok = slot >= 0 && (int64_t)slot < num_slots;
-  const int blk = ok ? slot / block_size : 0, off = ok ? slot % block_size : 0;
-  for (int j = threadIdx.x; j < per_tok; j += blockDim.x) {
-    const u32x4 a = load16(ks + (size_t)j * 16);
-    const u32x4 b = load16(vs + (size_t)j * 16);
-    if (!ok) continue;
-    const int h = j / chunks, c = j - h * chunks;
-    const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
-    store16(k_cache + dst, a);
-    store16(v_cache + dst, b);
-  }
+  scatter_token(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, num_kv_heads, chunks, block_size,
+                num_slots);
 }
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -51,6 +51,20 @@ bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int 
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                            int group, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
+
+// New tokens of a decode step (one per sequence), stored by the launch that
+// builds the work list.
+struct AppendArgs {
+  const char* k;              // [num_seqs, Hkv, D]
+  const char* v;
+  char* k_cache;
+  char* v_cache;
+  const int32_t* slot_mapping;  // [num_seqs]
+  int32_t chunks;             // 16-byte pieces per (token, head) row
+  int64_t num_slots;          // num_blocks * block_size
+};
+hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,
+                                  hipStream_t stream);
 bool launch_attention_reduce(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                              hipStream_t stream, hipError_t* err);
 

@@ -63,6 +63,32 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, m
                                                        ctypes.byref(opts)))
 
 
+def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads):
+    S, Hq, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("k_cache and v_cache must match each other and q's dtype")
+    if D2 != D or B != block_size or Hkv != num_kv_heads:
+        raise ValueError("cache shape disagrees with head_dim / block_size / num_kv_heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and context_lens [S]")
+
+
+def _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, device):
+    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel)
+    if need and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
+    return workspace
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, max_context_len, partition_size=0, kernel="auto",
                            workspace=None, stream=None, main_events=None):
@@ -75,27 +101,45 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     torch = _torch()
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
-    if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
-        raise ValueError("out must match q")
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("k_cache and v_cache must match each other and q's dtype")
-    if D2 != D or B != block_size or Hkv != num_kv_heads:
-        raise ValueError("cache shape disagrees with head_dim / block_size / num_kv_heads")
-    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("block_tables must be [S, M] and context_lens [S]")
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads)
     code = dtype_code(q)
-    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device)
     opts = _options(partition_size, kernel, main_events)
     st = lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         float(scale), B, Hkv, S, Hq, D, block_tables.shape[1], int(max_context_len), N, code,
-        ws_ptr, ws_len, ctypes.byref(opts), _stream(stream))
+        *_ws_args(workspace), ctypes.byref(opts), _stream(stream))
     check(st, "paged_attention_decode")
+    return out
+
+
+def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
+                block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
+                stream=None, main_events=None):
+    """reshape_and_cache(k_new, v_new, ..., slot_mapping) followed by
+    paged_attention_decode(...), with the token store and the attention work
+    list in one launch.  k_new, v_new: [S, Hkv, D]; slot_mapping int32 [S]."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads)
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("dtype mismatch")
+    if slot_mapping.shape != (S,):
+        raise ValueError("slot_mapping must be [num_seqs]")
+    code = dtype_code(q)
+    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device)
+    opts = _options(partition_size, kernel, main_events)
+    st = lib.pkv_decode_step(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), B, Hkv, S, Hq, D, block_tables.shape[1], int(max_context_len), N, code,
+        *_ws_args(workspace), ctypes.byref(opts), _stream(stream))
+    check(st, "decode_step")
     return out
 
 

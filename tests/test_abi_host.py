@@ -108,3 +108,26 @@ def test_scatter_and_copy_reject():
     assert L.pkv_copy_blocks(FAKE, FAKE, FAKE, -3, 2, 16, 64, 32, 0, None) == -2
     assert L.pkv_copy_blocks(None, None, None, 0, 2, 16, 64, 32, 0, None) == 0
     assert L.pkv_gather_kv(FAKE, FAKE, FAKE, FAKE, 2, 4, 64, 2, 2, 64, 16, 32, 0, None) == -2
+
+
+def test_decode_step_rejects():
+    L = pkv.lib
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, 16, 2, 4, 2, 64, 4, 64, 32, 0,
+            None, 0, None, None]
+
+    def call(**over):
+        a = list(args)
+        names = ["out", "q", "k_new", "v_new", "kc", "vc", "slots", "tables", "lens"]
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return L.pkv_decode_step(*a)
+
+    assert call(k_new=None) == -1
+    assert call(slots=None) == -1
+    assert call(v_new=ctypes.c_void_p(0x1004)) == -5
+    assert call(out=None) == -1
+    assert call() == -6                                             # workspace missing
+    a = list(args)
+    a[12] = 0                                                       # empty batch: nothing to do
+    a[:9] = [None] * 9
+    assert L.pkv_decode_step(*a) == 0

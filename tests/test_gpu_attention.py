@@ -215,3 +215,29 @@ def test_work_list_covers_every_partition_longest_first():
     rest = [size(x) for x in got[len(full):]]
     assert all(a >= b for a, b in zip(rest, rest[1:])), "last partitions must come longest first"
     assert rest[-2:] == [0, 0], "empty sequences come last"
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_decode_step_equals_scatter_then_attend(idx):
+    """The fused step stores the same bytes and returns the same bits as
+    reshape_and_cache followed by paged_attention_decode, and matches the
+    oracle."""
+    cfg = CONFIGS[idx] if idx == 1 else CONFIGS[idx].scaled(**SCALED[idx])
+    lay = make_layout(cfg, seed=60 + idx)
+    host = host_values(lay)
+    say(f"decode_step config {idx} S={len(lay.context_lens)}")
+    a = DeviceStep.from_host(lay, host)
+    b = DeviceStep.from_host(lay, host)
+    a.scatter()
+    out_a = a.attend(partition_size=cfg.partition_size)
+    out_b = torch.empty_like(b.q)
+    pkv.decode_step(out_b, b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.slots, b.tables, b.lens, cfg.scale,
+                    cfg.block_size, cfg.num_kv_heads, max(1, lay.max_context_len),
+                    partition_size=cfg.partition_size)
+    torch.cuda.synchronize()
+    view = torch.int32 if cfg.dtype == "f32" else torch.int16
+    assert torch.equal(a.k_cache.view(view), b.k_cache.view(view))
+    assert torch.equal(a.v_cache.view(view), b.v_cache.view(view))
+    assert torch.equal(out_a.view(view), out_b.view(view))
+    want, _, _ = oracle_step(lay, host)
+    assert_rows_close(widen(out_b), want, cfg.dtype, f"decode_step config {idx}")
