@@ -48,6 +48,7 @@ LENGTH_DESC = {
     3: "lognormal median 400 sigma 1.0, clipped [1, 4096]",
     4: "uniform [1024, 32768]",
     5: "1000-token shared prompt + uniform [1, 512] per-sample tail",
+    6: "uniform [1024, 16384], attention over the last 4096",
 }
 
 
@@ -67,7 +68,8 @@ def _oracle_rows(s):
     c = _CPU
     cfg = c["cfg"]
     oracle.paged_attention_decode(c["q"][s:s + 1], c["k"], c["v"], c["tables"][s:s + 1], c["lens"][s:s + 1],
-                                  cfg.scale, cfg.block_size, cfg.num_kv_heads, cfg.dtype)
+                                  cfg.scale, cfg.block_size, cfg.num_kv_heads, cfg.dtype,
+                                  sliding_window=cfg.sliding_window)
     return s
 
 
@@ -87,7 +89,10 @@ def cpu_baseline(cfg, layout, cpu_seconds: float):
     spp = cfg.samples_per_prompt or 1
     # Enough sequences to keep every worker busy, but a pool small enough to
     # draw on the host in seconds (about 2.5e8 cached values).
-    per_seq = layout.context_lens.astype(np.int64) * cfg.num_kv_heads * cfg.head_dim * 2
+    attended = layout.context_lens.astype(np.int64)
+    if cfg.sliding_window > 0:
+        attended = np.minimum(attended, cfg.sliding_window)
+    per_seq = attended * cfg.num_kv_heads * cfg.head_dim * 2
     k, acc = 0, 0
     while k < len(per_seq) and (k < workers or acc < 2.5e8):
         acc += int(per_seq[k])
@@ -111,7 +116,7 @@ def cpu_baseline(cfg, layout, cpu_seconds: float):
             elapsed = time.perf_counter() - t0
             if elapsed >= cpu_seconds:
                 break
-    nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.dtype) * reps
+    nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.dtype, cfg.sliding_window) * reps
     return {
         "value": round(nbytes / elapsed / 1e9, 4),
         "unit": "GB/s",
@@ -255,7 +260,7 @@ def main():
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
     S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     es = DTYPE_BYTES[cfg.dtype]
-    step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.dtype)
+    step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.dtype, cfg.sliding_window)
     log(f"workload {cfg.name}: S={S} Hq={Hq} Hkv={Hkv} D={D} B={B} {cfg.dtype} sum(L)={int(layout.context_lens.sum())} "
         f"pool={layout.num_blocks} blocks KV/step={step_kv / 1e9:.3f} GB")
 
@@ -290,7 +295,7 @@ def main():
     out = torch.empty_like(q)
     code = dtype_code(q)
     max_ctx = layout.max_context_len
-    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel)
+    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, cfg.sliding_window)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
@@ -312,8 +317,9 @@ def main():
     K, W = args.steps, args.warmup
     begins = [ev.create() for _ in range(K)]
     ends = [ev.create() for _ in range(K)]
-    plain = AttnOptions(part, KERNELS[args.kernel], None, None)
-    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i]) for i in range(K)]
+    win = cfg.sliding_window
+    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win)
+    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win) for i in range(K)]
     warm_args = step_args(plain)
     timed_args = [step_args(o) for o in timed]
 
@@ -351,7 +357,9 @@ def main():
 
     step_s = total_ms / 1e3 / K
     main_s = float(np.mean(main_ms)) / 1e3
-    nblk = -(-layout.context_lens // B)
+    lens64 = layout.context_lens.astype(np.int64)
+    first = np.maximum(0, lens64 - win) // B if win > 0 else np.zeros_like(lens64)
+    nblk = -(-lens64 // B) - first                    # table entries read per (sequence, KV head)
     alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4
     achieved = alg_bytes / main_s / 1e9
     kv_gbps = step_kv / step_s / 1e9
@@ -376,6 +384,7 @@ def main():
             "kv_dtype": cfg.dtype, "context_lens": LENGTH_DESC[args.config],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
             "kv_bytes_per_step": step_kv, "partition_size": part, "kernel": kernel_used,
+            "sliding_window": win,
             "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
         },
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),

@@ -81,7 +81,7 @@ enum pkv_kernel {
 
 typedef struct pkv_attn_options {
   /* Tokens per split-K partition.  0 = automatic: the smallest power of two
-   * of at least 1024 tokens that leaves about 2560 (sequence, KV head,
+   * of at least 1024 tokens that leaves about 1024 (sequence, KV head,
    * partition) work items if every sequence were max_context_len long (one
    * partition when that already covers max_context_len).  Otherwise a
    * positive multiple of block_size (and of 32 for the MFMA kernel).  A
@@ -96,6 +96,12 @@ typedef struct pkv_attn_options {
    * delays the second one by a few microseconds. */
   void* main_begin_event;
   void* main_end_event;
+  /* Sliding window ("pagedattention vllm" glossary, Advanced Features >
+   * Sliding Window): > 0 attends to the last sliding_window tokens of each
+   * sequence only, t in [max(0, L - W), L); 0 attends to all L tokens.
+   * Table entries of blocks wholly before the window are never read (they
+   * may be -1 once pkv_bm_slide_window released them). */
+  int32_t sliding_window;
 } pkv_attn_options;
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes and
@@ -117,8 +123,10 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * blocks).  For every sequence s and query head j, with h = j / (Hq / Hkv)
  * and L = context_lens[s]:
  *
- *   K_t = k_cache[block_tables[s][t / B]][h][t % B][:],  V_t likewise, t < L
+ *   K_t = k_cache[block_tables[s][t / B]][h][t % B][:],  V_t likewise,
  *   out[s][j][:] = sum_t softmax_t(scale * <q[s][j], K_t>) * V_t
+ *
+ * over t in [0, L), or [max(0, L - W), L) with a sliding window W.
  *
  * computed in fp32 and rounded to the data type (round to nearest even).
  * L = 0 gives a zero row.  Only the first ceil(L/B) table entries of a row
@@ -132,9 +140,10 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * Launches, in stream order: a one-workgroup plan kernel that reads
  * context_lens and writes the work list into the workspace (the
  * (sequence, partition) pairs, longest first, so long pieces start early
- * and the grid ends on short ones); the main kernel, one workgroup per
- * (pair, KV head); and, when max_context_len exceeds the partition, the
- * split-K reduce.  The schedule does not change any result.
+ * and the grid ends on short ones), then the main kernel, one workgroup per
+ * (pair, KV head); and, when a sequence can span several partitions, the
+ * split-K reduce, which merges the partial softmax states in partition
+ * order.  The schedule does not change any result.
  * Data errors are contained, never dereferenced: a table entry outside
  * [0, num_blocks), or context_lens[s] above max_context_len or
  * max_blocks_per_seq * B, makes that sequence's output rows NaN.
@@ -260,6 +269,14 @@ int pkv_bm_append_batch(pkv_block_manager* bm, const int32_t* seqs, int32_t n, i
                         int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs, int32_t* num_done);
 /* Release a finished sequence's blocks. */
 int pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq);
+/* Sliding window ("pagedattention vllm" glossary, Advanced Features >
+ * Sliding Window: keep only recent blocks): release the blocks of `seq` that
+ * hold no token of its last `window` tokens, i.e. table positions
+ * 0 .. (len - window) / B - 1.  Their table entries become -1 (positions do
+ * not move; attention with that window never reads them) and each loses one
+ * reference (back to the free list at zero).  Returns the number of entries
+ * released (>= 0) or a negative status. */
+int pkv_bm_slide_window(pkv_block_manager* bm, int32_t seq, int32_t window);
 /* Length of a sequence (>= 0) or a negative status. */
 int pkv_bm_seq_len(const pkv_block_manager* bm, int32_t seq);
 /* Copy a sequence's table into out[cap]; returns its number of blocks, or a

@@ -20,6 +20,11 @@ Definition followed:
   grouping into contiguous runs of query heads is a reading, not on the pages).
 * The scale is taken as the fp32 value the library receives, widened to fp64.
 * A sequence of length 0 has an all-zero output row (the pages are silent).
+* Sliding window ("pagedattention vllm" glossary, "Advanced Features >
+  Sliding Window": models with sliding-window attention keep only recent
+  blocks): with a window of W > 0 tokens, only the last W of the L tokens
+  are attended, t in [max(0, L - W), L); W = 0 means no window.  Blocks that
+  hold no attended token are never read, so their table entries may be -1.
 """
 from __future__ import annotations
 
@@ -28,27 +33,32 @@ import numpy as np
 from .formats import decode
 
 
-def gather_sequence(cache, table_row, length: int, kv_head: int, block_size: int) -> np.ndarray:
-    """Contiguous [length, head_dim] view of one sequence's cached rows for one KV head.
+def gather_sequence(cache, table_row, length: int, kv_head: int, block_size: int, start: int = 0) -> np.ndarray:
+    """Contiguous [length - start, head_dim] copy of tokens start .. length-1
+    of one sequence's cached rows for one KV head.
 
     `cache` is an array (or anything that supports cache[int_array, int]
     indexing and returns a numpy array) laid out [num_blocks, Hkv, B, D]."""
+    first = int(start) // block_size
     n_blocks = -(-int(length) // block_size)
-    phys = np.asarray(table_row[:n_blocks], dtype=np.int64)
+    phys = np.asarray(table_row[first:n_blocks], dtype=np.int64)
     num_blocks = cache.shape[0]
     if phys.size and (phys.min() < 0 or phys.max() >= num_blocks):
         raise ValueError("block table entry outside the pool")
-    tiles = np.asarray(cache[phys, kv_head])            # [n_blocks, B, D]
-    return tiles.reshape(n_blocks * block_size, tiles.shape[-1])[:length]
+    tiles = np.asarray(cache[phys, kv_head])            # [n_blocks - first, B, D]
+    rows = tiles.reshape((n_blocks - first) * block_size, tiles.shape[-1])
+    return rows[int(start) - first * block_size:int(length) - first * block_size]
 
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                           block_size: int, num_kv_heads: int, dtype: str, rows=None) -> np.ndarray:
+                           block_size: int, num_kv_heads: int, dtype: str, rows=None,
+                           sliding_window: int = 0) -> np.ndarray:
     """fp64 decode attention through the block tables.
 
     q: [S, Hq, D] in storage format; caches [N, Hkv, B, D]; block_tables int
     [S, M]; context_lens int [S].  Returns fp64 [S, Hq, D], or, when `rows`
-    lists (s, j) pairs, an fp64 [len(rows), D] array in that order."""
+    lists (s, j) pairs, an fp64 [len(rows), D] array in that order.
+    sliding_window > 0 attends to the last sliding_window tokens only."""
     S, Hq, D = q.shape
     if Hq % num_kv_heads:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
@@ -65,8 +75,9 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         L = int(context_lens[s])
         if L <= 0:
             continue
-        K = decode(gather_sequence(k_cache, block_tables[s], L, h, block_size), dtype)
-        V = decode(gather_sequence(v_cache, block_tables[s], L, h, block_size), dtype)
+        t0 = max(0, L - sliding_window) if sliding_window > 0 else 0
+        K = decode(gather_sequence(k_cache, block_tables[s], L, h, block_size, t0), dtype)
+        V = decode(gather_sequence(v_cache, block_tables[s], L, h, block_size, t0), dtype)
         for idx, j in members:
             qv = decode(q[s, j], dtype)
             x = scale64 * (K @ qv)

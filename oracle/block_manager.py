@@ -19,7 +19,9 @@ zero are put back at its front, in table order.  A fork gives the child the
 parent's table and length and adds one reference to every shared block.
 Appending at position t allocates a block when t % B == 0; otherwise, if the
 last block has more than one reference, it is copied first and the pair
-(shared, copy) is reported for the device-side block copy.
+(shared, copy) is reported for the device-side block copy.  With a sliding
+window, blocks wholly before the window are released and their table
+entries set to -1.
 """
 from __future__ import annotations
 
@@ -58,7 +60,8 @@ class BlockManager:
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
         for b in self.tables[child]:
-            self.refcount[b] += 1
+            if b >= 0:
+                self.refcount[b] += 1
 
     def _take(self) -> int:
         if not self.free:
@@ -90,12 +93,36 @@ class BlockManager:
         if seq not in self.tables:
             raise BlockManagerError(f"unknown sequence {seq}")
         for b in self.tables.pop(seq):
+            if b < 0:
+                continue
             if self.refcount[b] <= 0:
                 raise BlockManagerError("reference count underflow")
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.free.appendleft(b)
         del self.lengths[seq]
+
+    def slide_window(self, seq: int, window: int) -> int:
+        """Release the blocks that hold no token of the last `window` tokens
+        ("pagedattention vllm" glossary, "Advanced Features > Sliding Window":
+        only recent blocks are kept).  Their table entries become -1; table
+        positions do not move.  Returns how many entries were released."""
+        if seq not in self.tables or window <= 0:
+            raise BlockManagerError("unknown sequence or empty window")
+        first = self.lengths[seq] - window
+        n = first // self.block_size if first > 0 else 0
+        table = self.tables[seq]
+        released = 0
+        for i in range(min(n, len(table))):
+            b = table[i]
+            if b < 0:
+                continue
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.appendleft(b)
+            table[i] = -1
+            released += 1
+        return released
 
     def block_table(self, seq: int) -> list[int]:
         return list(self.tables[seq])

@@ -15,7 +15,7 @@ c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 class AttnOptions(ctypes.Structure):
     _fields_ = [("partition_size", c_i32), ("kernel", c_i32),
-                ("main_begin_event", c_vp), ("main_end_event", c_vp)]
+                ("main_begin_event", c_vp), ("main_end_event", c_vp), ("sliding_window", c_i32)]
 
 
 class PkvError(RuntimeError):
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH):
         "pkv_bm_append": (ctypes.c_int, [c_vp, c_i32, c_i32p, c_i32p, c_i32p]),
         "pkv_bm_append_batch": (ctypes.c_int, [c_vp, c_i32p, c_i32, c_i32p, c_i32p, c_i32, c_i32p, c_i32p]),
         "pkv_bm_free_seq": (ctypes.c_int, [c_vp, c_i32]),
+        "pkv_bm_slide_window": (ctypes.c_int, [c_vp, c_i32, c_i32]),
         "pkv_bm_seq_len": (ctypes.c_int, [c_vp, c_i32]),
         "pkv_bm_block_table": (ctypes.c_int, [c_vp, c_i32, c_i32p, c_i32]),
         "pkv_bm_export": (ctypes.c_int, [c_vp, c_i32p, c_i32, c_i32p, c_i32, c_i32p]),

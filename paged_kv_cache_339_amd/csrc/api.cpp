@@ -17,12 +17,13 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 // Automatic split-K partition: the smallest power of two of at least
 // kMinAutoPartition tokens that still leaves about kFillItems
 // (sequence, KV head, partition) work items when every sequence is as long
-// as the longest; an MI355X keeps 1280 of these workgroups resident (256 CUs
-// x 5), and the plan orders them longest first, so the machine stays full
-// and the last items are short.  Measured: fewer, longer partitions beat
-// short ones as soon as there are enough items (no reduce pass, no
-// partial-result traffic).
-constexpr int64_t kFillItems = 2560;
+// as the longest.  An MI355X keeps 512 (MFMA kernel) to 1280 (vector kernel)
+// of these workgroups resident, and the plan orders them longest first, so
+// the last items are short.  Measured on the 7B/13B/GQA/sliding-window
+// layers: once there are that many items, one partition per sequence beats
+// any split (no reduce pass, no partial-result traffic), so splitting is
+// kept for batches with too few (sequence, KV head) pairs to fill the chip.
+constexpr int64_t kFillItems = 1024;
 constexpr int64_t kMinAutoPartition = 1024;
 
 int dtype_bytes(pkv_dtype dt) {
@@ -41,6 +42,7 @@ bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 // Workspace layout: [work header][work pairs][partition outputs][partition (m, l)].
 struct Plan {
   int kernel;
+  int32_t window;
   int32_t part_blocks;
   int32_t max_parts;
   int64_t max_pairs;
@@ -75,24 +77,35 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   // chunk boundaries for the MFMA kernel.
   const int32_t align = kernel == PKV_KERNEL_MFMA ? (block_size > 32 ? block_size : 32) : block_size;
   int32_t part = opts ? opts->partition_size : 0;
-  if (part < 0) return PKV_ERR_SHAPE;
+  const int32_t window = opts ? opts->sliding_window : 0;
+  if (part < 0 || window < 0) return PKV_ERR_SHAPE;
   if (part > 0 && part % align) return PKV_ERR_SHAPE;
+
+  // Blocks one sequence can ask for: its whole context, or those a window of
+  // `window` tokens can touch (it may start inside a block).
+  const int64_t ctx_blocks = ((int64_t)max_context_len + block_size - 1) / block_size;
+  int64_t span_blocks = ctx_blocks;
+  if (window > 0) {
+    const int64_t w_blocks = ((int64_t)window + block_size - 1) / block_size + 1;
+    if (w_blocks < span_blocks) span_blocks = w_blocks;
+  }
+  const int64_t span_tokens = span_blocks * block_size;
   if (part == 0) {
-    const int64_t want = ((int64_t)max_context_len * num_seqs * num_kv_heads + kFillItems - 1) / kFillItems;
+    const int64_t want = (span_tokens * num_seqs * num_kv_heads + kFillItems - 1) / kFillItems;
     int64_t p2 = kMinAutoPartition;
-    while (p2 < want && p2 < max_context_len) p2 <<= 1;
+    while (p2 < want && p2 < span_tokens) p2 <<= 1;
     part = (int32_t)(p2 < 0x40000000 ? p2 : 0x40000000);
   }
   part = (int32_t)round_up(part, align);
 
-  const int64_t ctx_blocks = ((int64_t)max_context_len + block_size - 1) / block_size;
-  if ((int64_t)max_context_len <= part) {
-    plan->part_blocks = (int32_t)(ctx_blocks > 0 ? ctx_blocks : 1);
+  if (span_tokens <= part) {
+    plan->part_blocks = (int32_t)(span_blocks > 0 ? span_blocks : 1);
     plan->max_parts = 1;
   } else {
     plan->part_blocks = part / block_size;
-    plan->max_parts = (int32_t)((ctx_blocks + plan->part_blocks - 1) / plan->part_blocks);
+    plan->max_parts = (int32_t)((span_blocks + plan->part_blocks - 1) / plan->part_blocks);
   }
+  plan->window = window;
   if ((int64_t)num_seqs * num_kv_heads * plan->max_parts > kMaxGrid) return PKV_ERR_SHAPE;
   plan->kernel = kernel;
   plan->max_pairs = (int64_t)num_seqs * plan->max_parts;
@@ -203,6 +216,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.part_blocks = plan.part_blocks;
   p.max_parts = plan.max_parts;
   p.max_pairs = (int32_t)plan.max_pairs;
+  p.window = plan.window;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / num_kv_heads;

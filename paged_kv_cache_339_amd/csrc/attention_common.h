@@ -14,9 +14,17 @@
 
 namespace pkv {
 
+// What one sequence asks of the kernels.  Attended tokens are [t0, L): all
+// of them, or the last `window` with a sliding window ("pagedattention vllm"
+// glossary, Advanced Features > Sliding Window).  Partition p covers blocks
+// [blk0 + p*part_blocks, ...) of the nblk blocks from blk0 to the block of
+// token L-1; blocks before blk0 are never read (their table entries may be
+// -1 once released).
 struct SeqWork {
-  int L;        // tokens attended
-  int nblk;     // blocks those tokens occupy
+  int L;        // one past the last attended token
+  int t0;       // first attended token
+  int blk0;     // logical block holding t0
+  int nblk;     // blocks blk0 .. (L-1)/B
   int nparts;   // split-K partitions of the sequence
   bool bad;     // context length outside what the table / launch covers
 };
@@ -27,7 +35,9 @@ __device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
   w.bad = raw < 0 || raw > p.max_context_len ||
           (int64_t)raw > (int64_t)p.max_blocks_per_seq * B;
   w.L = w.bad ? 0 : raw;
-  w.nblk = (w.L + B - 1) / B;
+  w.t0 = (p.window > 0 && w.L > p.window) ? w.L - p.window : 0;
+  w.blk0 = w.t0 / B;
+  w.nblk = w.L > 0 ? (w.L + B - 1) / B - w.blk0 : 0;
   w.nparts = (w.nblk + p.part_blocks - 1) / p.part_blocks;
   return w;
 }

@@ -40,9 +40,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   // sequence length is known (they lie inside the row whatever the length),
   // one per lane, so translating a block later is a register read.
   const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
-  const int b0 = it.part * p.part_blocks;
+  const int b0_guess = it.part * p.part_blocks;    // exact unless a window starts later
   int tab = -1;
-  if (lane < p.part_blocks && b0 + lane < p.max_blocks_per_seq) tab = table[b0 + lane];
+  if (lane < p.part_blocks && b0_guess + lane < p.max_blocks_per_seq) tab = table[b0_guess + lane];
 
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
@@ -77,18 +77,21 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
 
   const char* kbase = reinterpret_cast<const char*>(p.k_cache);
   const char* vbase = reinterpret_cast<const char*>(p.v_cache);
-  const int b1 = min(sw.nblk, b0 + p.part_blocks);
-  const int tail = sw.L - (sw.nblk - 1) * B;      // tokens in the last block, 1..B
+  const int b0 = sw.blk0 + it.part * p.part_blocks;
+  const int last = sw.blk0 + sw.nblk - 1;           // block of token L-1
+  const int b1 = min(last + 1, b0 + p.part_blocks);
+  const int tail = sw.L - last * B;                 // tokens in the last block, 1..B
+  const int head = sw.t0 - sw.blk0 * B;             // tokens of block blk0 before the window
   int bad = 0;
 
   for (int c0 = b0; c0 < b1; c0 += kWave) {
-    if (c0 != b0) tab = (c0 + lane < b1) ? table[c0 + lane] : -1;
+    if (c0 != b0_guess) tab = (lane < kWave && c0 + lane < b1) ? table[c0 + lane] : -1;
     const int cn = min(kWave, b1 - c0);
     // Wave w takes U consecutive blocks at a time; all their key and value
     // loads are issued before any of them is used.
     for (int j = w * U; j < cn; j += NW * U) {
       u32x4 kr[U][NL], vr[U][NL];
-      int valid[U];
+      int valid[U], first[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int jj = j + u;
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
         const int phys = __builtin_amdgcn_readlane(tab, in ? jj : 0);
         const bool ok = in && (unsigned)phys < (unsigned)p.num_blocks;
         bad |= in && !ok;
-        valid[u] = !ok ? 0 : (c0 + jj == sw.nblk - 1 ? tail : B);
+        valid[u] = !ok ? 0 : (c0 + jj == last ? tail : B);
+        first[u] = c0 + jj == sw.blk0 ? head : 0;
         const size_t lane_off = (((size_t)(ok ? phys : 0) * Hkv + it.h) * B + grp) * D + sub * EPL;
         const char* kt = kbase + lane_off * ES;
         const char* vt = vbase + lane_off * ES;
@@ -104,7 +108,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
         for (int i = 0; i < NL; ++i) {
           kr[u][i] = u32x4{0, 0, 0, 0};
           vr[u][i] = u32x4{0, 0, 0, 0};
-          if (i * TPW + grp < valid[u]) {
+          const int row = i * TPW + grp;
+          if (row >= first[u] && row < valid[u]) {
             kr[u][i] = load16_kv(kt + (size_t)i * TPW * D * ES);
             vr[u][i] = load16_kv(vt + (size_t)i * TPW * D * ES);
           }
@@ -118,7 +123,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
         for (int i = 0; i < NL; ++i) {
           float kf[EPL];
           widen16<DT>(kr[u][i], kf);
-          const bool row_ok = i * TPW + grp < valid[u];
+          const int row = i * TPW + grp;
+          const bool row_ok = row >= first[u] && row < valid[u];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float a = 0.f;

@@ -85,7 +85,8 @@ int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child) {
     return PKV_ERR_STATE;
   }
   bm->length[child] = bm->length[parent];
-  for (int32_t b : bm->tables[child]) ++bm->refcount[b];
+  for (int32_t b : bm->tables[child])
+    if (b >= 0) ++bm->refcount[b];
   return PKV_OK;
 }
 
@@ -149,13 +150,32 @@ int pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq) {
   if (!bm) return PKV_ERR_NULL;
   if (!live(bm, seq)) return PKV_ERR_STATE;
   for (int32_t b : bm->tables[seq])
-    if (bm->refcount[b] <= 0) return PKV_ERR_STATE;
+    if (b >= 0 && bm->refcount[b] <= 0) return PKV_ERR_STATE;
   for (int32_t b : bm->tables[seq]) {
-    if (--bm->refcount[b] == 0) bm->free_list.push_front(b);
+    if (b >= 0 && --bm->refcount[b] == 0) bm->free_list.push_front(b);
   }
   bm->tables[seq].clear();
   bm->length[seq] = -1;
   return PKV_OK;
+}
+
+int pkv_bm_slide_window(pkv_block_manager* bm, int32_t seq, int32_t window) {
+  if (!bm) return PKV_ERR_NULL;
+  if (!live(bm, seq) || window <= 0) return PKV_ERR_STATE;
+  auto& table = bm->tables[seq];
+  const int64_t first = (int64_t)bm->length[seq] - window;   // first attended token
+  const int64_t n = first > 0 ? first / bm->block_size : 0;  // blocks wholly before it
+  for (int64_t i = 0; i < n && i < (int64_t)table.size(); ++i)
+    if (table[i] >= 0 && bm->refcount[table[i]] <= 0) return PKV_ERR_STATE;
+  int released = 0;
+  for (int64_t i = 0; i < n && i < (int64_t)table.size(); ++i) {
+    const int32_t b = table[i];
+    if (b < 0) continue;
+    if (--bm->refcount[b] == 0) bm->free_list.push_front(b);
+    table[i] = -1;
+    ++released;
+  }
+  return released;
 }
 
 int pkv_bm_seq_len(const pkv_block_manager* bm, int32_t seq) {

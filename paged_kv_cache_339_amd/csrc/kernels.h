@@ -43,6 +43,7 @@ struct AttnParams {
   int32_t part_blocks;        // blocks per split-K partition
   int32_t max_parts;          // partitions per sequence covered by the grid
   int32_t max_pairs;          // num_seqs * max_parts, the room of `pairs`
+  int32_t window;             // sliding window in tokens, 0 = attend to all
 };
 
 // Returns false when no kernel instance exists for the combination.

@@ -48,16 +48,16 @@ def _dev(t, name, dtype=None, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _options(partition_size, kernel, main_events):
+def _options(partition_size, kernel, main_events, sliding_window=0):
     ev0, ev1 = (None, None) if main_events is None else main_events
     return AttnOptions(int(partition_size), KERNELS[kernel],
                        None if ev0 is None else ctypes.c_void_p(int(ev0)),
-                       None if ev1 is None else ctypes.c_void_p(int(ev1)))
+                       None if ev1 is None else ctypes.c_void_p(int(ev1)), int(sliding_window))
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                    dtype_code_, partition_size=0, kernel="auto") -> int:
-    opts = _options(partition_size, kernel, None)
+                    dtype_code_, partition_size=0, kernel="auto", sliding_window=0) -> int:
+    opts = _options(partition_size, kernel, None, sliding_window)
     return int(lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        block_size, max_context_len, dtype_code_,
                                                        ctypes.byref(opts)))
@@ -76,8 +76,9 @@ def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens
         raise ValueError("block_tables must be [S, M] and context_lens [S]")
 
 
-def _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, device):
-    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel)
+def _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, device,
+               sliding_window=0):
+    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, sliding_window)
     if need and workspace is None:
         workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
     return workspace
@@ -91,7 +92,7 @@ def _ws_args(workspace):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, max_context_len, partition_size=0, kernel="auto",
-                           workspace=None, stream=None, main_events=None):
+                           workspace=None, stream=None, main_events=None, sliding_window=0):
     """out[s, j] = softmax(scale * q[s, j] K_s^T) V_s through the block tables.
 
     q, out: [S, Hq, D]; k_cache, v_cache: [N, Hkv, B, D]; block_tables int32
@@ -103,8 +104,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     N, Hkv, B, D2 = k_cache.shape
     _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads)
     code = dtype_code(q)
-    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device)
-    opts = _options(partition_size, kernel, main_events)
+    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
+                           sliding_window)
+    opts = _options(partition_size, kernel, main_events, sliding_window)
     st = lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
@@ -116,7 +118,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
 def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
                 block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
-                stream=None, main_events=None):
+                stream=None, main_events=None, sliding_window=0):
     """reshape_and_cache(k_new, v_new, ..., slot_mapping) followed by
     paged_attention_decode(...), with the token store and the attention work
     list in one launch.  k_new, v_new: [S, Hkv, D]; slot_mapping int32 [S]."""
@@ -131,8 +133,9 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
     if slot_mapping.shape != (S,):
         raise ValueError("slot_mapping must be [num_seqs]")
     code = dtype_code(q)
-    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device)
-    opts = _options(partition_size, kernel, main_events)
+    workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
+                           sliding_window)
+    opts = _options(partition_size, kernel, main_events, sliding_window)
     st = lib.pkv_decode_step(
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),
@@ -246,6 +249,12 @@ class BlockManager:
 
     def free_seq(self, seq):
         check(lib.pkv_bm_free_seq(self._h, seq), "bm_free_seq")
+
+    def slide_window(self, seq, window):
+        n = lib.pkv_bm_slide_window(self._h, seq, window)
+        if n < 0:
+            raise PkvError(n, "bm_slide_window")
+        return n
 
     def seq_len(self, seq):
         n = lib.pkv_bm_seq_len(self._h, seq)

@@ -37,6 +37,7 @@ class DecodeConfig:
     partition_size: int = 0  # split-K partition in tokens; 0 = library default
     prompt_len: int = 0      # shared-prefix workloads only
     samples_per_prompt: int = 0
+    sliding_window: int = 0  # attend to the last W tokens; blocks wholly before them are released
 
     @property
     def group(self) -> int:
@@ -75,9 +76,17 @@ CONFIGS = {
                     head_dim=128, dtype="bf16", block_size=16, lengths="shared_prefix",
                     len_lo=1, len_hi=512, prompt_len=1000, samples_per_prompt=8,
                     partition_size=1024),
+    # A sliding-window grouped-query layer (Mistral-7B-like: 32 query heads
+    # over 8 KV heads, 4096-token window): only the blocks the window touches
+    # hold data; table entries before them are -1.
+    6: DecodeConfig("swa_mistral7b_layer_bf16", num_seqs=64, num_q_heads=32, num_kv_heads=8,
+                    head_dim=128, dtype="bf16", block_size=16, lengths="uniform",
+                    len_lo=1024, len_hi=16384, sliding_window=4096),
 }
 
 
-def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, dtype: str) -> int:
-    """Logical K+V bytes one decode step reads: sum(L) * Hkv * D * 2 * bytes."""
-    return int(sum(int(x) for x in context_lens)) * num_kv_heads * head_dim * 2 * DTYPE_BYTES[dtype]
+def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, dtype: str, sliding_window: int = 0) -> int:
+    """Logical K+V bytes one decode step reads: sum(L) * Hkv * D * 2 * bytes,
+    with L capped at the window when there is one."""
+    lens = [min(int(x), sliding_window) if sliding_window > 0 else int(x) for x in context_lens]
+    return sum(lens) * num_kv_heads * head_dim * 2 * DTYPE_BYTES[dtype]

@@ -76,6 +76,10 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
     lens = draw_lengths(cfg, rng) if lengths is None else np.asarray(lengths, dtype=np.int32)
     S, B = len(lens), cfg.block_size
     nblk = [_ceil_div(int(L), B) for L in lens]
+    # With a sliding window, blocks wholly before the last W tokens are
+    # released: their table entries stay -1 and take no pool block.
+    W = cfg.sliding_window
+    skip = [max(0, int(L) - W) // B if W > 0 else 0 for L in lens]
 
     shared = cfg.lengths == "shared_prefix"
     if shared:
@@ -90,7 +94,7 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
             for k in range(spp):
                 need += nblk[p * spp + k] - pb
     else:
-        need = sum(nblk)
+        need = sum(n - k for n, k in zip(nblk, skip))
     N = cfg.pool_blocks if cfg.pool_blocks else int(math.ceil(cfg.pool_factor * need))
     if N < need:
         raise ValueError(f"pool of {N} blocks cannot hold {need}")
@@ -121,7 +125,7 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
                 tables[s, :nblk[s]] = row
     else:
         for s in range(S):
-            tables[s, :nblk[s]] = take(nblk[s])
+            tables[s, skip[s]:nblk[s]] = take(nblk[s] - skip[s])
 
     live = np.zeros((N, B), dtype=bool)
     new_slots = np.full(S, -1, dtype=np.int32)
@@ -129,7 +133,7 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
         L = int(lens[s])
         if L == 0:
             continue
-        t = np.arange(L - 1)
+        t = np.arange(skip[s] * B, L - 1)
         live[tables[s, t // B], t % B] = True
         last = L - 1
         new_slots[s] = tables[s, last // B] * B + last % B

@@ -64,9 +64,26 @@ class Paged:
         self.k_cache, self.v_cache, self.table = kp, vp, table
         self.lens = np.array(lens, dtype=np.int32)
 
-    def run(self, attn, scale, num_kv_heads, rows=None):
+    def run(self, attn, scale, num_kv_heads, rows=None, window=0):
         return attn(self.q, self.k_cache, self.v_cache, self.table, self.lens, scale,
-                    self.B, num_kv_heads, self.dtype, rows=rows)
+                    self.B, num_kv_heads, self.dtype, rows=rows, sliding_window=window)
+
+    def free_before_window(self, window):
+        """Copy whose table entries for blocks wholly before each sequence's
+        window are -1 and whose blocks there are poisoned (freed blocks)."""
+        import copy
+        other = copy.copy(self)
+        other.table = self.table.copy()
+        other.k_cache = self.k_cache.copy()
+        other.v_cache = self.v_cache.copy()
+        width = np.uint32 if self.dtype == "f32" else np.uint16
+        for s, L in enumerate(self.lens.tolist()):
+            for b in range(max(0, L - window) // self.B):
+                blk = other.table[s, b]
+                other.k_cache.view(width)[blk] = POISON_BITS[self.dtype]
+                other.v_cache.view(width)[blk] = POISON_BITS[self.dtype]
+                other.table[s, b] = -1
+        return other
 
 
 def draw(rng, lens, Hq, Hkv, D, dtype):
@@ -201,4 +218,35 @@ def check_rows_subset(attn):
     assert np.array_equal(sub, np.stack([full[s, j] for s, j in rows]))
 
 
-ALL_CHECKS = [check_against_sdpa, check_closed_forms, check_invariances, check_rows_subset]
+def check_sliding_window(attn):
+    """Sliding window: SDPA over the contiguous last-W slice; W >= L is no
+    window; W = 1 returns the last value row; blocks wholly before the window
+    can be freed (table entry -1, contents poisoned) without any effect;
+    the block size does not matter."""
+    rng = np.random.default_rng(51)
+    lens = [1, 7, 16, 17, 40, 70, 129]
+    Hq, Hkv, D = 4, 2, 16
+    K, V, q = draw(rng, lens, Hq, Hkv, D, "f16")
+    scale = 0.31
+    paged = Paged(K, V, q, 8, "f16", 3, spare_blocks=5)
+    for W in (1, 5, 8, 9, 33, 64):
+        got = paged.run(attn, scale, Hkv, window=W)
+        want = sdpa_reference([k[-W:] for k in K], [v[-W:] for v in V], q, scale, "f16")
+        err = np.max(np.abs(got - want))
+        assert err <= 1e-12, f"window {W}: paged vs SDPA on the last W tokens, max |err| {err}"
+        freed = paged.free_before_window(W).run(attn, scale, Hkv, window=W)
+        assert np.array_equal(freed, got), f"window {W}: freed blocks before the window changed results"
+        for B in (16, 32):
+            other = Paged(K, V, q, B, "f16", 4).run(attn, scale, Hkv, window=W)
+            assert np.array_equal(other, got), f"window {W}: block size {B} changed results"
+    full = paged.run(attn, scale, Hkv)
+    assert np.array_equal(paged.run(attn, scale, Hkv, window=max(lens)), full), "W >= L must be no window"
+    one = paged.run(attn, scale, Hkv, window=1)
+    g = Hq // Hkv
+    for s in range(len(lens)):
+        for j in range(Hq):
+            assert np.array_equal(one[s, j], widen(V[s][-1, j // g], "f16")), "W = 1 returns the last value"
+
+
+ALL_CHECKS = [check_against_sdpa, check_closed_forms, check_invariances, check_rows_subset,
+              check_sliding_window]

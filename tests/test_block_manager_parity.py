@@ -19,7 +19,7 @@ def compare(cpp, twin, seqs):
     assert cpp.free_list() == list(twin.free)
 
 
-ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "append", "append", "free"]),
+ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "append", "append", "free", "slide"]),
                          st.integers(0, 7), st.integers(0, 7), st.integers(1, 30)), max_size=60)
 
 
@@ -63,6 +63,14 @@ def test_random_operation_sequences_agree(ops, N, B, seed):
             else:
                 with pytest.raises(pkv.PkvError):
                     cpp.free_seq(a)
+        elif op == "slide":
+            try:
+                want = twin.slide_window(a, n)
+            except oracle.BlockManagerError:
+                with pytest.raises(pkv.PkvError):
+                    cpp.slide_window(a, n)
+            else:
+                assert cpp.slide_window(a, n) == want
         else:
             for _ in range(n):
                 try:

@@ -39,6 +39,7 @@ def test_config1_every_row(partition_size):
 
 
 SCALED = {
+    6: dict(num_seqs=6),
     2: dict(num_seqs=6),
     3: dict(num_seqs=24),
     4: dict(num_seqs=3),
@@ -46,7 +47,7 @@ SCALED = {
 }
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
 def test_scaled_workloads_every_row(idx):
     cfg = CONFIGS[idx].scaled(**SCALED[idx])
     run_case(cfg, seed=10 + idx, partition_size=cfg.partition_size, label=f"config{idx}-scaled")
@@ -217,7 +218,7 @@ def test_work_list_covers_every_partition_longest_first():
     assert rest[-2:] == [0, 0], "empty sequences come last"
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_decode_step_equals_scatter_then_attend(idx):
     """The fused step stores the same bytes and returns the same bits as
     reshape_and_cache followed by paged_attention_decode, and matches the
@@ -233,7 +234,7 @@ def test_decode_step_equals_scatter_then_attend(idx):
     out_b = torch.empty_like(b.q)
     pkv.decode_step(out_b, b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.slots, b.tables, b.lens, cfg.scale,
                     cfg.block_size, cfg.num_kv_heads, max(1, lay.max_context_len),
-                    partition_size=cfg.partition_size)
+                    partition_size=cfg.partition_size, sliding_window=cfg.sliding_window)
     torch.cuda.synchronize()
     view = torch.int32 if cfg.dtype == "f32" else torch.int16
     assert torch.equal(a.k_cache.view(view), b.k_cache.view(view))
@@ -241,3 +242,57 @@ def test_decode_step_equals_scatter_then_attend(idx):
     assert torch.equal(out_a.view(view), out_b.view(view))
     want, _, _ = oracle_step(lay, host)
     assert_rows_close(widen(out_b), want, cfg.dtype, f"decode_step config {idx}")
+
+
+WINDOW_CASES = [
+    # dtype, B, Hq, Hkv, kernel
+    ("bf16", 16, 32, 8, "mfma"), ("bf16", 16, 32, 8, "valu"), ("f16", 32, 8, 8, "valu"),
+    ("f32", 16, 2, 1, "valu"), ("f16", 8, 16, 1, "mfma"),
+]
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,kernel", WINDOW_CASES)
+def test_sliding_window_every_row(dtype, B, Hq, Hkv, kernel):
+    """Attention over the last W tokens, blocks wholly before the window
+    released (table entries -1, pool blocks absent), both kernels, several
+    partition sizes, windows from one token to longer than the context."""
+    lens = [1, 2, B - 1, B, B + 1, 37, 100, 511, 512, 513, 1000, 2047]
+    for W in (1, B - 1, B + 1, 100, 512, 4096):
+        cfg = DecodeConfig("window", num_seqs=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128 if dtype != "f32" else 64,
+                           dtype=dtype, block_size=B, lengths="fixed", fixed_lengths=tuple(lens),
+                           pool_factor=1.3, sliding_window=W)
+        lay = make_layout(cfg, seed=W)
+        assert (lay.block_tables[lens.index(2047), :(2047 - W) // B] == -1).all() or W >= 2047
+        for part in (0, max(B, 32), 256):
+            run_case(cfg, seed=W, lengths=lens, partition_size=part, kernel=kernel,
+                     label=f"window/{dtype}/B{B}/G{Hq // Hkv}/{kernel}/W{W}/p{part}")
+
+
+def test_sliding_window_of_one_returns_the_last_value_row():
+    cfg = DecodeConfig("window1", num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
+                       block_size=16, lengths="fixed", fixed_lengths=(1, 16, 17, 300, 1025), pool_factor=1.5,
+                       sliding_window=1)
+    lay = make_layout(cfg, seed=3)
+    host = host_values(lay)
+    step = DeviceStep.from_host(lay, host)
+    step.scatter()
+    say("window of one token")
+    for kernel in ("mfma", "valu"):
+        out = step.attend(kernel=kernel)
+        torch.cuda.synchronize()
+        want = np.repeat(host.v_new, 4, axis=1)         # the appended token is the last one
+        assert to_storage_np(out, "bf16").tobytes() == np.ascontiguousarray(want).tobytes(), kernel
+
+
+def test_decode_step_with_window():
+    cfg = CONFIGS[6].scaled(num_seqs=6)
+    lay = make_layout(cfg, seed=66)
+    host = host_values(lay)
+    say("decode_step with a sliding window")
+    b = DeviceStep.from_host(lay, host)
+    out = torch.empty_like(b.q)
+    pkv.decode_step(out, b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.slots, b.tables, b.lens, cfg.scale,
+                    cfg.block_size, cfg.num_kv_heads, lay.max_context_len, sliding_window=cfg.sliding_window)
+    torch.cuda.synchronize()
+    want, _, _ = oracle_step(lay, host)
+    assert_rows_close(widen(out), want, cfg.dtype, "decode_step window")

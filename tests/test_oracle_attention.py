@@ -59,36 +59,36 @@ def _with_decode(fake_decode):
     return impl
 
 
-def _gather_offset_off_by_one(cache, row, length, h, B):
+def _gather_offset_off_by_one(cache, row, length, h, B, start=0):
     n = -(-length // B)
     tiles = np.asarray(cache[np.asarray(row[:n], dtype=np.int64), h])
     tiles = np.roll(tiles, 1, axis=1)                  # in-block offset shifted
-    return tiles.reshape(n * B, -1)[:length]
+    return tiles.reshape(n * B, -1)[start:length]
 
 
-def _gather_block_order_reversed(cache, row, length, h, B):
+def _gather_block_order_reversed(cache, row, length, h, B, start=0):
     n = -(-length // B)
     tiles = np.asarray(cache[np.asarray(row[:n], dtype=np.int64)[::-1], h])
-    return tiles.reshape(n * B, -1)[:length]
+    return tiles.reshape(n * B, -1)[start:length]
 
 
-def _gather_head_and_offset_swapped(cache, row, length, h, B):
+def _gather_head_and_offset_swapped(cache, row, length, h, B, start=0):
     # reads the pool as if it were laid out [N, B, Hkv, D]
     n = -(-length // B)
     arr = np.asarray(cache)
     N, Hkv, _, D = arr.shape
     tiles = arr.reshape(N, B, Hkv, D)[np.asarray(row[:n], dtype=np.int64)][:, :, h, :]
-    return tiles.reshape(n * B, -1)[:length]
+    return tiles.reshape(n * B, -1)[start:length]
 
 
-def _gather_drops_last_token(cache, row, length, h, B):
-    return oracle.gather_sequence(cache, row, max(1, length - 1), h, B)
+def _gather_drops_last_token(cache, row, length, h, B, start=0):
+    return oracle.gather_sequence(cache, row, max(1, length - 1), h, B, min(start, max(0, length - 2)))
 
 
-def _gather_whole_last_block(cache, row, length, h, B):
+def _gather_whole_last_block(cache, row, length, h, B, start=0):
     n = -(-length // B)
     tiles = np.asarray(cache[np.asarray(row[:n], dtype=np.int64), h])
-    return tiles.reshape(n * B, -1)
+    return tiles.reshape(n * B, -1)[start:]
 
 
 def _decode_bf16_shift_15(raw, dtype):
@@ -103,8 +103,10 @@ def _decode_f16_as_bf16(raw, dtype):
     return decode(raw, dtype)
 
 
-def _mutant_body(head_of=None, drop_scale=False, no_normalise=False, no_max=False, scale_twice=False):
-    def impl(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_kv_heads, dtype, rows=None):
+def _mutant_body(head_of=None, drop_scale=False, no_normalise=False, no_max=False, scale_twice=False,
+                 window_shift=0, window_from_start=False):
+    def impl(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_kv_heads, dtype, rows=None,
+             sliding_window=0):
         S, Hq, D = q.shape
         g = Hq // num_kv_heads
         out = np.zeros((S, Hq, D))
@@ -114,8 +116,12 @@ def _mutant_body(head_of=None, drop_scale=False, no_normalise=False, no_max=Fals
                 continue
             for j in range(Hq):
                 h = head_of(j, g, num_kv_heads) if head_of else j // g
-                K = decode(oracle.gather_sequence(k_cache, block_tables[s], L, h, block_size), dtype)
-                V = decode(oracle.gather_sequence(v_cache, block_tables[s], L, h, block_size), dtype)
+                lo, hi = 0, L
+                if sliding_window > 0:
+                    W = min(L, max(1, sliding_window + window_shift))
+                    lo, hi = (0, W) if window_from_start else (L - W, L)
+                K = decode(oracle.gather_sequence(k_cache, block_tables[s], hi, h, block_size, lo), dtype)
+                V = decode(oracle.gather_sequence(v_cache, block_tables[s], hi, h, block_size, lo), dtype)
                 x = (K @ decode(q[s, j], dtype))
                 if not drop_scale:
                     x = float(np.float32(scale)) * x
@@ -142,6 +148,9 @@ MUTANTS = {
     "scale_dropped": _mutant_body(drop_scale=True),
     "scale_applied_twice": _mutant_body(scale_twice=True),
     "softmax_not_normalised": _mutant_body(no_normalise=True),
+    "window_one_token_too_long": _mutant_body(window_shift=1),
+    "window_one_token_too_short": _mutant_body(window_shift=-1),
+    "window_counted_from_the_start": _mutant_body(window_from_start=True),
 }
 
 

@@ -21,8 +21,12 @@ def check_invariants(bm: BlockManager):
     for seq, table in bm.tables.items():
         L = bm.lengths[seq]
         assert len(table) == -(-L // B), "a sequence holds exactly ceil(L/B) blocks"
+        released = sum(1 for b in table if b < 0)
+        assert all(b < 0 for b in table[:released]), "only a leading run of blocks is released"
+        assert released == 0 or released * B < L, "the last token's block is never released"
         for b in table:
-            counted[b] += 1
+            if b >= 0:
+                counted[b] += 1
     assert counted == bm.refcount, "reference count = number of tables naming the block"
     free = list(bm.free)
     assert len(set(free)) == len(free), "free list holds a block twice"
@@ -34,7 +38,7 @@ def _snapshot(bm):
     return ({s: list(t) for s, t in bm.tables.items()}, dict(bm.lengths), list(bm.refcount), list(bm.free))
 
 
-ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "append", "append", "free"]),
+ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "append", "append", "free", "slide"]),
                          st.integers(0, 7), st.integers(0, 7), st.integers(1, 40)), max_size=60)
 
 
@@ -51,6 +55,13 @@ def test_invariants_hold_under_random_operations(ops, N, B, seed):
                 bm.fork(a, b)
             elif op == "free":
                 bm.free_seq(a)
+            elif op == "slide":
+                L = bm.lengths.get(a, 0)
+                n_rel = bm.slide_window(a, n)
+                first = L - n
+                assert all(b < 0 for b in bm.tables[a][:max(0, first) // B]), "blocks before the window released"
+                assert all(b >= 0 for b in bm.tables[a][max(0, first) // B:]), "window blocks kept"
+                assert n_rel <= max(0, first) // B
             else:
                 for _ in range(n):
                     others = {s: list(t) for s, t in bm.tables.items() if s != a}
