@@ -83,7 +83,7 @@ typedef struct pkv_attn_options {
   /* Tokens per split-K partition.  0 = automatic: the smallest power of two
    * of at least 1024 tokens that leaves about 1024 (sequence, KV head,
    * partition) work items if every sequence were max_context_len long (one
-   * partition when that already covers max_context_len).  Otherwise a
+   * partition when that, plus a quarter, covers the longest span).  Otherwise a
    * positive multiple of block_size (and of 32 for the MFMA kernel).  A
    * sequence of length L is cut into ceil(L / partition_size) partitions
    * that separate workgroups process; a reduce kernel merges them. */

@@ -94,6 +94,9 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
     const int64_t want = (span_tokens * num_seqs * num_kv_heads + kFillItems - 1) / kFillItems;
     int64_t p2 = kMinAutoPartition;
     while (p2 < want && p2 < span_tokens) p2 <<= 1;
+    // A span just past a power of two (a window that starts inside a block)
+    // stays one partition rather than leaving a sliver for a second one.
+    if (span_tokens <= p2 + p2 / 4) p2 = span_tokens;
     part = (int32_t)(p2 < 0x40000000 ? p2 : 0x40000000);
   }
   part = (int32_t)round_up(part, align);

@@ -131,3 +131,16 @@ def test_decode_step_rejects():
     a[12] = 0                                                       # empty batch: nothing to do
     a[:9] = [None] * 9
     assert L.pkv_decode_step(*a) == 0
+
+
+def test_automatic_partition_splits_only_small_batches():
+    """With the longest-first work list, one partition per sequence is kept
+    whenever there are enough (sequence, KV head) pairs; only a batch too
+    small to fill the chip is split (partial results appear in the
+    workspace)."""
+    ws = pkv.workspace_bytes
+    one = lambda S: 256 + _up(S * 8)
+    assert ws(64, 32, 32, 128, 16, 2048, 1) == one(64)                        # 2048 pairs
+    assert ws(256, 64, 8, 128, 32, 32768, 2) == one(256)                      # 2048 pairs, 32k tokens
+    assert ws(64, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == one(64)  # window span 4112 tokens
+    assert ws(4, 8, 8, 128, 16, 32768, 2) > one(4 * 32)                       # 32 pairs: split
