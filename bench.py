@@ -38,7 +38,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synthetic import CONFIGS, DTYPE_BYTES, host_values, kv_bytes, make_layout  # noqa: E402
+from synthetic import (BEAM_CONFIGS, CONFIGS, DTYPE_BYTES, beam_parents, host_values, kv_bytes,  # noqa: E402
+                       make_layout)
 
 METRIC = "paged decode attn: KV GB/s read (% of HBM peak) + seq·heads/sec, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
@@ -228,12 +229,195 @@ def calibrate_copy(launches: int):
                       "write_bytes_per_launch": per}), flush=True)
 
 
+def beam_cpu_baseline(cfg, cpu_seconds: float):
+    """The oracle (block-manager twin, bitwise copy and scatter, fp64
+    attention) running the same beam search on host arrays, one core, for a
+    bounded number of steps of a 2-request slice of the workload."""
+    import oracle
+    from synthetic import POISON_BITS, prompt_values, step_values
+
+    sub = cfg.scaled(num_requests=2)
+    R, W, B, Hkv, D = sub.num_requests, sub.beam_width, sub.block_size, sub.num_kv_heads, sub.head_dim
+    N = sub.pool_blocks()
+    width = np.uint32 if sub.dtype == "f32" else np.uint16
+    storage = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[sub.dtype]
+    kc = np.full((N, Hkv, B, D), POISON_BITS[sub.dtype], dtype=width).view(storage)
+    vc = kc.copy()
+    bm = oracle.BlockManager(N, B, np.random.default_rng(0).permutation(N))
+    pk, pv = prompt_values(sub, 0)
+    for r in range(R):
+        bm.add_seq(r * W)
+        slots = [bm.append(r * W)[0] for _ in range(sub.prompt_len)]
+        oracle.reshape_and_cache(pk[r], pv[r], kc, vc, np.array(slots), B)
+    parents = beam_parents(sub, 0)
+    bank, nbytes, steps, t0 = 0, 0, 0, time.perf_counter()
+    while steps < sub.steps and time.perf_counter() - t0 < cpu_seconds:
+        old = list(range(bank * R * W, (bank + 1) * R * W))
+        new = list(range((1 - bank) * R * W, (2 - bank) * R * W))
+        for r in range(R):
+            for b in range(W):
+                bm.fork(old[r * W + (0 if steps == 0 else int(parents[steps, r, b]))], new[r * W + b])
+        for r in range(R):
+            for b in range(W):
+                if steps > 0 or b == 0:
+                    bm.free_seq(old[r * W + b])
+        bank = 1 - bank
+        slots, pairs = [], []
+        for sq in new:
+            slot, cow = bm.append(sq)
+            slots.append(slot)
+            if cow is not None:
+                pairs.append(cow)
+        if pairs:
+            oracle.copy_blocks(kc, vc, pairs)
+        q, kn, vn = step_values(sub, 0, steps)
+        oracle.reshape_and_cache(kn, vn, kc, vc, np.array(slots), B)
+        M = max(len(bm.block_table(sq)) for sq in new)
+        tables = np.full((len(new), M), -1, dtype=np.int32)
+        for i, sq in enumerate(new):
+            tables[i, :len(bm.block_table(sq))] = bm.block_table(sq)
+        lens = np.array([bm.seq_len(sq) for sq in new])
+        oracle.paged_attention_decode(q, kc, vc, tables, lens, sub.scale, B, Hkv, sub.dtype)
+        nbytes += kv_bytes(lens, Hkv, D, sub.dtype)
+        steps += 1
+    elapsed = time.perf_counter() - t0
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{R} of {cfg.num_requests} requests x {W} beams, {steps} search steps "
+                       f"(block manager twin, copy, scatter, fp64 attention), one process, {elapsed:.2f} s")}
+
+
+def beam_bench(args):
+    """Beam search over the paged cache: each timed step is the host control
+    plane (fork the chosen parents, free the old beams, reserve slots and
+    copy-on-write pairs), the copies of tables / slots / pairs to the GPU,
+    pkv_copy_blocks and pkv_decode_step, then a stream synchronisation (a
+    real search reads the step's scores before choosing parents)."""
+    import torch
+    import paged_kv_cache_339_amd as pkv
+    from paged_kv_cache_339_amd._lib import AttnOptions, lib
+    from paged_kv_cache_339_amd.ops import dtype_code
+
+    K, W = args.steps, args.warmup
+    base = BEAM_CONFIGS[args.config]
+    cfg = base.scaled(steps=max(base.steps, K + W))
+    seed = args.config if args.seed is None else args.seed
+    R, Wb, B, Hq, Hkv, D = cfg.num_requests, cfg.beam_width, cfg.block_size, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    S, N = cfg.num_seqs, cfg.pool_blocks()
+    es = DTYPE_BYTES[cfg.dtype]
+    log(f"beam workload {cfg.name}: {R} requests x {Wb} beams, prompt {cfg.prompt_len}, pool {N} blocks")
+    cpu = None if args.no_cpu_baseline else beam_cpu_baseline(base, args.cpu_seconds)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    kc = torch.randn((N, Hkv, B, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    vc = torch.randn((N, Hkv, B, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    total = K + W
+    qs = torch.randn((total, S, Hq, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    ks = torch.randn((total, S, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    vs = torch.randn((total, S, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    parents = beam_parents(cfg, seed)
+    cache = pkv.BeamSearchCache(R, Wb, N, B, np.random.default_rng(seed).permutation(N))
+    prompt_slots = cache.prefill(cfg.prompt_len)
+    for r in range(R):
+        pk = torch.randn((cfg.prompt_len, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        pv = torch.randn((cfg.prompt_len, Hkv, D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        pkv.reshape_and_cache(pk, pv, kc, vc, torch.from_numpy(prompt_slots[r]).to(dev))
+    M = -(-(cfg.prompt_len + cfg.steps + 1) // B)
+    max_ctx = cfg.prompt_len + cfg.steps + 1
+    code = dtype_code(kc)
+    ws = torch.empty(max(256, pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
+    pin = dict(tables=torch.empty((S, M), dtype=torch.int32).pin_memory(),
+               lens=torch.empty(S, dtype=torch.int32).pin_memory(),
+               slots=torch.empty(S, dtype=torch.int32).pin_memory(),
+               pairs=torch.empty((S, 2), dtype=torch.int32).pin_memory())
+    dbuf = {k: torch.empty(v.shape, dtype=torch.int32, device=dev) for k, v in pin.items()}
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    vp = ctypes.c_void_p
+    begins = [ev.create() for _ in range(total)]
+    ends = [ev.create() for _ in range(total)]
+    step_start = [ev.create() for _ in range(total)]
+    step_end = [ev.create() for _ in range(total)]
+    kv_step = []
+    host_s = []
+
+    def step(t):
+        h0 = time.perf_counter()
+        _, slots, pairs = cache.step(parents[t])
+        tables, lens = cache.tables(M)
+        host_s.append(time.perf_counter() - h0)
+        pin["tables"].numpy()[:] = tables
+        pin["lens"].numpy()[:] = lens
+        pin["slots"].numpy()[:] = slots
+        n_pairs = len(pairs)
+        if n_pairs:
+            pin["pairs"].numpy()[:n_pairs] = pairs
+        ev.record(step_start[t], stream.cuda_stream)
+        for k in dbuf:
+            dbuf[k].copy_(pin[k], non_blocking=True)
+        if n_pairs:
+            st = lib.pkv_copy_blocks(vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["pairs"].data_ptr()), n_pairs,
+                                     Hkv, B, D, N, code, vp(stream.cuda_stream))
+            assert st == 0, st
+        opts = AttnOptions(0, 0, begins[t], ends[t], 0)
+        st = lib.pkv_decode_step(vp(out.data_ptr()), vp(qs[t].data_ptr()), vp(ks[t].data_ptr()), vp(vs[t].data_ptr()),
+                                 vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["slots"].data_ptr()),
+                                 vp(dbuf["tables"].data_ptr()), vp(dbuf["lens"].data_ptr()), cfg.scale, B, Hkv, S,
+                                 Hq, D, M, max_ctx, N, code, vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
+                                 vp(stream.cuda_stream))
+        assert st == 0, st
+        ev.record(step_end[t], stream.cuda_stream)
+        stream.synchronize()
+        kv_step.append(kv_bytes(lens, Hkv, D, cfg.dtype))
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for t in range(W, total):
+        step(t)
+    wall = time.perf_counter() - wall0
+    gpu_ms = [ev.ms(step_start[t], step_end[t]) for t in range(W, total)]
+    main_ms = [ev.ms(begins[t], ends[t]) for t in range(W, total)]
+    ev.close()
+    cache.close()
+    assert torch.isfinite(out.float()).all().item(), "non-finite attention output"
+    kv = float(np.mean(kv_step[W:]))
+    step_s = wall / K
+    main_s = float(np.mean(main_ms)) / 1e3
+    alg = kv + 2 * S * Hq * D * es + S * M * 4 * Hkv + S * 4
+    print(json.dumps({
+        "metric": METRIC, "value": round(kv / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": R, "beam_width": Wb, "prompt_len": cfg.prompt_len,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B, "kv_dtype": cfg.dtype,
+                   "pool_blocks": N, "kv_bytes_per_step": int(kv),
+                   "step": "host fork/free/append + H2D tables + copy_blocks + decode_step + sync"},
+        "pct_hbm_peak": round(100 * kv / step_s / 1e9 / HBM_PEAK_GBPS, 2),
+        "seq_heads_per_s": round(S * Hq / step_s, 1),
+        "host_ms_per_step": round(1e3 * float(np.mean(host_s[W:])), 4),
+        "gpu_ms_per_step": round(float(np.mean(gpu_ms)), 4),
+        "roofline": {"bound": "hbm", "achieved": round(alg / main_s / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(alg / main_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "attn_valu_kernel", "bytes_per_launch": int(alg),
+                     "note": "logical bytes: the beams of a request share their prompt blocks, served from cache"},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS) + sorted(BEAM_CONFIGS))
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="split-K partition in tokens (0 = library default; -1 = the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
@@ -252,6 +436,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.steps)
+        return
+    if args.config in BEAM_CONFIGS:
+        beam_bench(args)
         return
 
     cfg = CONFIGS[args.config]

@@ -256,6 +256,13 @@ void pkv_bm_destroy(pkv_block_manager* bm);
 int pkv_bm_add_seq(pkv_block_manager* bm, int32_t seq);
 /* child gets parent's table and length; each shared block gains a reference */
 int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child);
+/* children[i] = fork of parents[i] for i in order (beam search: every new
+ * beam continues a chosen parent).  On an error at i the forks before i
+ * stay done, *num_done = i, and the error is returned. */
+int pkv_bm_fork_batch(pkv_block_manager* bm, const int32_t* parents, const int32_t* children,
+                      int32_t n, int32_t* num_done);
+/* pkv_bm_free_seq for each of seqs[0..n), in order; errors as fork_batch. */
+int pkv_bm_free_batch(pkv_block_manager* bm, const int32_t* seqs, int32_t n, int32_t* num_done);
 /* Reserve the next token's slot.  *cow_src / *cow_dst receive the pair to
  * copy before the write, or -1 / -1.  PKV_ERR_NO_BLOCKS leaves all state
  * unchanged. */

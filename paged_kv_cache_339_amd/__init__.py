@@ -13,6 +13,7 @@ import ctypes
 import os
 
 from ._lib import LIB_PATH, PkvError, check, lib
+from .beam import BeamSearchCache
 from .ops import (
     BlockManager,
     copy_blocks,
@@ -24,6 +25,6 @@ from .ops import (
 )
 
 __all__ = [
-    "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
+    "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
     "paged_attention_decode", "reshape_and_cache", "workspace_bytes",
 ]

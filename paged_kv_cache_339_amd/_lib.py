@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH):
         "pkv_bm_append": (ctypes.c_int, [c_vp, c_i32, c_i32p, c_i32p, c_i32p]),
         "pkv_bm_append_batch": (ctypes.c_int, [c_vp, c_i32p, c_i32, c_i32p, c_i32p, c_i32, c_i32p, c_i32p]),
         "pkv_bm_free_seq": (ctypes.c_int, [c_vp, c_i32]),
+        "pkv_bm_fork_batch": (ctypes.c_int, [c_vp, c_i32p, c_i32p, c_i32, c_i32p]),
+        "pkv_bm_free_batch": (ctypes.c_int, [c_vp, c_i32p, c_i32, c_i32p]),
         "pkv_bm_slide_window": (ctypes.c_int, [c_vp, c_i32, c_i32]),
         "pkv_bm_seq_len": (ctypes.c_int, [c_vp, c_i32]),
         "pkv_bm_block_table": (ctypes.c_int, [c_vp, c_i32, c_i32p, c_i32]),

@@ -90,6 +90,31 @@ int pkv_bm_fork(pkv_block_manager* bm, int32_t parent, int32_t child) {
   return PKV_OK;
 }
 
+int pkv_bm_fork_batch(pkv_block_manager* bm, const int32_t* parents, const int32_t* children,
+                      int32_t n, int32_t* num_done) {
+  if (!bm || !num_done || (n > 0 && (!parents || !children))) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_SHAPE;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int st = pkv_bm_fork(bm, parents[i], children[i]);
+    if (st != PKV_OK) return st;
+    *num_done = i + 1;
+  }
+  return PKV_OK;
+}
+
+int pkv_bm_free_batch(pkv_block_manager* bm, const int32_t* seqs, int32_t n, int32_t* num_done) {
+  if (!bm || !num_done || (n > 0 && !seqs)) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_SHAPE;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int st = pkv_bm_free_seq(bm, seqs[i]);
+    if (st != PKV_OK) return st;
+    *num_done = i + 1;
+  }
+  return PKV_OK;
+}
+
 int pkv_bm_append(pkv_block_manager* bm, int32_t seq, int32_t* slot, int32_t* cow_src,
                   int32_t* cow_dst) {
   if (!bm || !slot || !cow_src || !cow_dst) return PKV_ERR_NULL;

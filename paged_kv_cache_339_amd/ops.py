@@ -227,6 +227,27 @@ class BlockManager:
     def fork(self, parent, child):
         check(lib.pkv_bm_fork(self._h, parent, child), "bm_fork")
 
+    def fork_batch(self, parents, children):
+        pa, pp = _i32(parents)
+        ca, cp = _i32(children)
+        if pa.shape != ca.shape:
+            raise ValueError("parents and children must have the same length")
+        done = ctypes.c_int32()
+        st = lib.pkv_bm_fork_batch(self._h, pp, cp, len(pa), ctypes.byref(done))
+        if st != 0:
+            err = PkvError(st, "bm_fork_batch")
+            err.num_done = done.value
+            raise err
+
+    def free_batch(self, seqs):
+        sa, sp = _i32(seqs)
+        done = ctypes.c_int32()
+        st = lib.pkv_bm_free_batch(self._h, sp, len(sa), ctypes.byref(done))
+        if st != 0:
+            err = PkvError(st, "bm_free_batch")
+            err.num_done = done.value
+            raise err
+
     def append(self, seq):
         slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         check(lib.pkv_bm_append(self._h, seq, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)),

@@ -7,8 +7,10 @@ placement and N(0, 1) values.
 from .configs import CONFIGS, DTYPE_BYTES, DecodeConfig, kv_bytes
 from .layout import Layout, draw_lengths, make_layout
 from .values import POISON_BITS, HostStep, device_values, host_values, to_storage
+from .beam import BEAM_CONFIGS, BeamConfig, beam_parents, prompt_values, step_values
 
 __all__ = [
     "CONFIGS", "DTYPE_BYTES", "DecodeConfig", "kv_bytes", "Layout", "draw_lengths",
     "make_layout", "POISON_BITS", "HostStep", "device_values", "host_values", "to_storage",
+    "BEAM_CONFIGS", "BeamConfig", "beam_parents", "prompt_values", "step_values",
 ]
