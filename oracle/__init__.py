@@ -19,8 +19,9 @@ What it follows (page, section):
 * chipfoundryservices glossary "pagedattention vllm", "Attention Computation"
   (Block-Wise Attention, Address Translation), "Copy-on-Write Sharing"
   (Reference Counting, Divergence Handling), "Memory Management" (Block
-  Allocation) and "Implementation Details" (Metadata Overhead: 4-byte table
-  entries).
+  Allocation), "Implementation Details" (Metadata Overhead: 4-byte table
+  entries), "Advanced Features" (Sliding Window) and "Comparison with
+  Alternatives" (vs Compression: an 8-bit E4M3 cache with per-tensor scales).
 
 Every function here is pinned by tests that do not re-type its formula:
 torch's scaled-dot-product attention on independently laid-out data, closed
@@ -28,12 +29,13 @@ forms, exact invariances under block placement, block size, batch order and
 copy-on-write, exhaustive format decoding, and the pages' worked numbers.
 No function is "parity unpinned".
 """
-from .formats import decode
+from .formats import E4M3_MAX, decode, decode_e4m3, quantize_e4m3
 from .attention import gather_sequence, paged_attention_decode
-from .cache_ops import copy_blocks, reshape_and_cache
+from .cache_ops import copy_blocks, reshape_and_cache, reshape_and_cache_fp8
 from .block_manager import BlockManager, NoFreeBlocks, BlockManagerError
 
 __all__ = [
+    "E4M3_MAX", "decode", "decode_e4m3", "quantize_e4m3", "reshape_and_cache_fp8",
     "decode", "gather_sequence", "paged_attention_decode", "copy_blocks", "reshape_and_cache",
     "BlockManager", "NoFreeBlocks", "BlockManagerError",
 ]

@@ -20,6 +20,10 @@ Definition followed:
   grouping into contiguous runs of query heads is a reading, not on the pages).
 * The scale is taken as the fp32 value the library receives, widened to fp64.
 * A sequence of length 0 has an all-zero output row (the pages are silent).
+* 8-bit cache ("pagedattention vllm" glossary, "Comparison with Alternatives
+  > vs Compression"): with kv_format "fp8_e4m3" the caches hold E4M3 codes
+  and a key or value is e4m3(code) * k_scale (or v_scale), the scales taken
+  as the fp32 values the library receives; q keeps its own format.
 * Sliding window ("pagedattention vllm" glossary, "Advanced Features >
   Sliding Window": models with sliding-window attention keep only recent
   blocks): with a window of W > 0 tokens, only the last W of the L tokens
@@ -30,7 +34,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode
+from .formats import decode, decode_e4m3
 
 
 def gather_sequence(cache, table_row, length: int, kv_head: int, block_size: int, start: int = 0) -> np.ndarray:
@@ -52,7 +56,8 @@ def gather_sequence(cache, table_row, length: int, kv_head: int, block_size: int
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
                            block_size: int, num_kv_heads: int, dtype: str, rows=None,
-                           sliding_window: int = 0) -> np.ndarray:
+                           sliding_window: int = 0, kv_format: str = "same", k_scale: float = 1.0,
+                           v_scale: float = 1.0) -> np.ndarray:
     """fp64 decode attention through the block tables.
 
     q: [S, Hq, D] in storage format; caches [N, Hkv, B, D]; block_tables int
@@ -76,8 +81,15 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         if L <= 0:
             continue
         t0 = max(0, L - sliding_window) if sliding_window > 0 else 0
-        K = decode(gather_sequence(k_cache, block_tables[s], L, h, block_size, t0), dtype)
-        V = decode(gather_sequence(v_cache, block_tables[s], L, h, block_size, t0), dtype)
+        Kraw = gather_sequence(k_cache, block_tables[s], L, h, block_size, t0)
+        Vraw = gather_sequence(v_cache, block_tables[s], L, h, block_size, t0)
+        if kv_format == "fp8_e4m3":
+            K = decode_e4m3(Kraw) * float(np.float32(k_scale))
+            V = decode_e4m3(Vraw) * float(np.float32(v_scale))
+        elif kv_format == "same":
+            K, V = decode(Kraw, dtype), decode(Vraw, dtype)
+        else:
+            raise ValueError(f"unknown kv_format {kv_format!r}")
         for idx, j in members:
             qv = decode(q[s, j], dtype)
             x = scale64 * (K @ qv)

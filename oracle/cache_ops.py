@@ -4,6 +4,9 @@
   block the block table names ("What is PagedAttention" (tecyfy), "How it
   works"): token i goes to block slot_mapping[i] // B at offset
   slot_mapping[i] % B, all KV heads; a negative slot means "do not store".
+* reshape_and_cache_fp8: the same store into a cache of 8-bit E4M3 codes with
+  a per-tensor scale (paging combined with quantization, "pagedattention
+  vllm" glossary, "Comparison with Alternatives > vs Compression").
 * copy_blocks: the copy made before a shared block is modified
   ("pagedattention vllm" glossary, "Copy-on-Write Sharing > Divergence
   Handling"): for each (src, dst) pair, block dst of both caches becomes a
@@ -16,6 +19,8 @@ depend on the order pairs are applied in.
 from __future__ import annotations
 
 import numpy as np
+
+from .formats import decode, quantize_e4m3
 
 
 def _bits(a: np.ndarray) -> np.ndarray:
@@ -49,3 +54,23 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
             raise ValueError("block id outside the pool")
         kc[dst] = kc[src]
         vc[dst] = vc[src]
+
+
+def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, block_size: int, k_scale: float,
+                          v_scale: float, dtype: str) -> None:
+    """In place, into caches of E4M3 codes (uint8 [N, Hkv, B, D]).  Each new
+    value x (storage format `dtype`) is stored as the code of
+    fp32(x) / fp32(scale), the division in fp32 (the precision the decision
+    is taken in on both sides), rounded by quantize_e4m3; negative slots
+    are skipped."""
+    kq = quantize_e4m3(decode(k, dtype).astype(np.float32) / np.float32(k_scale))
+    vq = quantize_e4m3(decode(v, dtype).astype(np.float32) / np.float32(v_scale))
+    num_blocks = k_cache.shape[0]
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, block_size)
+        if block >= num_blocks:
+            raise ValueError(f"slot {slot} outside the pool")
+        k_cache[block, :, offset, :] = kq[i]
+        v_cache[block, :, offset, :] = vq[i]

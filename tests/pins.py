@@ -43,9 +43,10 @@ class Paged:
         perm = rng.permutation(N)
         table = np.full((S, max(1, max(nb))), -1, dtype=np.int32)
         storage = K[0].dtype
-        width = np.uint32 if dtype == "f32" else np.uint16
-        kp = np.full((N, Hkv, block_size, D), POISON_BITS[dtype], dtype=width).view(storage)
-        vp = np.full((N, Hkv, block_size, D), POISON_BITS[dtype], dtype=width).view(storage)
+        width = {"f32": np.uint32, "fp8": np.uint8}.get(dtype, np.uint16)
+        poison = 0xFF if dtype == "fp8" else POISON_BITS[dtype]
+        kp = np.full((N, Hkv, block_size, D), poison, dtype=width).view(storage)
+        vp = np.full((N, Hkv, block_size, D), poison, dtype=width).view(storage)
         pos = 0
         for s in range(S):
             if share is not None and share.get(s) is not None:
@@ -93,13 +94,16 @@ def draw(rng, lens, Hq, Hkv, D, dtype):
     return K, V, q
 
 
-def sdpa_reference(K, V, q, scale, dtype):
-    """torch's scaled-dot-product attention, fp64, on the contiguous sequences."""
+def sdpa_reference(K, V, q, scale, dtype, values_are_fp64=False):
+    """torch's scaled-dot-product attention, fp64, on the contiguous sequences
+    (K, V in storage format `dtype`, or already fp64 with values_are_fp64)."""
     S, Hq, D = q.shape
     out = np.zeros((S, Hq, D))
     for s in range(S):
-        k = torch.from_numpy(widen(K[s], dtype)).permute(1, 0, 2)    # [Hkv, L, D]
-        v = torch.from_numpy(widen(V[s], dtype)).permute(1, 0, 2)
+        kk = K[s] if values_are_fp64 else widen(K[s], dtype)
+        vv = V[s] if values_are_fp64 else widen(V[s], dtype)
+        k = torch.from_numpy(np.ascontiguousarray(kk)).permute(1, 0, 2)    # [Hkv, L, D]
+        v = torch.from_numpy(np.ascontiguousarray(vv)).permute(1, 0, 2)
         g = Hq // k.shape[0]
         k = k.repeat_interleave(g, dim=0).contiguous()
         v = v.repeat_interleave(g, dim=0).contiguous()
@@ -248,5 +252,48 @@ def check_sliding_window(attn):
             assert np.array_equal(one[s, j], widen(V[s][-1, j // g], "f16")), "W = 1 returns the last value"
 
 
+def fp8_paged(rng, lens, Hq, Hkv, D, B, placement_seed, q_dtype="f16"):
+    """A batch whose cache holds random finite E4M3 codes (placed like Paged)."""
+    K = [rng.integers(0, 0x7F, size=(L, Hkv, D)).astype(np.uint8) | (rng.integers(0, 2, size=(L, Hkv, D)) * 0x80).astype(np.uint8)
+         for L in lens]
+    V = [rng.integers(0, 0x7F, size=(L, Hkv, D)).astype(np.uint8) | (rng.integers(0, 2, size=(L, Hkv, D)) * 0x80).astype(np.uint8)
+         for L in lens]
+    # keep magnitudes moderate: codes of exponent field <= 9 (|value| < 8)
+    K = [np.where(((k >> 3) & 15) > 9, k & 0x87, k).astype(np.uint8) for k in K]
+    V = [np.where(((v >> 3) & 15) > 9, v & 0x87, v).astype(np.uint8) for v in V]
+    q = to_storage(rng.standard_normal((len(lens), Hq, D)), q_dtype)
+    p = Paged(K, V, q, B, "fp8", placement_seed)
+    return p, K, V, q
+
+
+def torch_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_fp8_kv(attn):
+    """8-bit cache: SDPA on torch's decoding of the codes times the scales;
+    scaling v_scale by 2 doubles the output exactly; placement and block
+    size change nothing."""
+    rng = np.random.default_rng(61)
+    lens = [1, 9, 16, 33, 70]
+    Hq, Hkv, D = 4, 2, 16
+    p, K, V, q = fp8_paged(rng, lens, Hq, Hkv, D, 8, 1)
+    ks, vs, scale = 0.375, 0.0625, 0.25
+
+    def run(paged, **kw):
+        return attn(paged.q, paged.k_cache, paged.v_cache, paged.table, paged.lens, scale, paged.B, Hkv, "f16",
+                    kv_format="fp8_e4m3", **kw)
+
+    got = run(p, k_scale=ks, v_scale=vs)
+    Kf = [torch_e4m3(k) * ks for k in K]
+    Vf = [torch_e4m3(v) * vs for v in V]
+    want = sdpa_reference(Kf, Vf, q, scale, "f16", values_are_fp64=True)
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-12, f"fp8 cache vs SDPA on dequantized values: {err}"
+    assert np.array_equal(run(p, k_scale=ks, v_scale=2 * vs), 2 * got), "v_scale must scale the output"
+    other = Paged(K, V, q, 16, "fp8", 9, spare_blocks=7)
+    assert np.array_equal(run(other, k_scale=ks, v_scale=vs), got), "placement / block size changed results"
+
+
 ALL_CHECKS = [check_against_sdpa, check_closed_forms, check_invariances, check_rows_subset,
-              check_sliding_window]
+              check_sliding_window, check_fp8_kv]

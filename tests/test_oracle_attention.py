@@ -103,10 +103,16 @@ def _decode_f16_as_bf16(raw, dtype):
     return decode(raw, dtype)
 
 
+def _fnuz_like_decode(codes):
+    """E4M3 decoded with exponent bias 8 (another 8-bit format's convention)."""
+    return oracle.decode_e4m3(codes) / 2.0
+
+
 def _mutant_body(head_of=None, drop_scale=False, no_normalise=False, no_max=False, scale_twice=False,
-                 window_shift=0, window_from_start=False):
+                 window_shift=0, window_from_start=False, ignore_k_scale=False, ignore_v_scale=False,
+                 fp8_decode=None):
     def impl(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_kv_heads, dtype, rows=None,
-             sliding_window=0):
+             sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
         S, Hq, D = q.shape
         g = Hq // num_kv_heads
         out = np.zeros((S, Hq, D))
@@ -120,8 +126,14 @@ def _mutant_body(head_of=None, drop_scale=False, no_normalise=False, no_max=Fals
                 if sliding_window > 0:
                     W = min(L, max(1, sliding_window + window_shift))
                     lo, hi = (0, W) if window_from_start else (L - W, L)
-                K = decode(oracle.gather_sequence(k_cache, block_tables[s], hi, h, block_size, lo), dtype)
-                V = decode(oracle.gather_sequence(v_cache, block_tables[s], hi, h, block_size, lo), dtype)
+                Kr = oracle.gather_sequence(k_cache, block_tables[s], hi, h, block_size, lo)
+                Vr = oracle.gather_sequence(v_cache, block_tables[s], hi, h, block_size, lo)
+                if kv_format == "fp8_e4m3":
+                    dec = fp8_decode or oracle.decode_e4m3
+                    K = dec(Kr) * (1.0 if ignore_k_scale else float(np.float32(k_scale)))
+                    V = dec(Vr) * (1.0 if ignore_v_scale else float(np.float32(v_scale)))
+                else:
+                    K, V = decode(Kr, dtype), decode(Vr, dtype)
                 x = (K @ decode(q[s, j], dtype))
                 if not drop_scale:
                     x = float(np.float32(scale)) * x
@@ -151,6 +163,9 @@ MUTANTS = {
     "window_one_token_too_long": _mutant_body(window_shift=1),
     "window_one_token_too_short": _mutant_body(window_shift=-1),
     "window_counted_from_the_start": _mutant_body(window_from_start=True),
+    "fp8_k_scale_ignored": _mutant_body(ignore_k_scale=True),
+    "fp8_v_scale_ignored": _mutant_body(ignore_v_scale=True),
+    "fp8_decoded_with_bias_8": _mutant_body(fp8_decode=_fnuz_like_decode),
 }
 
 

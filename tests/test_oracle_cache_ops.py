@@ -88,3 +88,32 @@ def test_copy_blocks_rejects_ambiguous_pairs():
         oracle.copy_blocks(kc, kc.copy(), [(0, 1), (2, 1)])     # duplicate destination
     with pytest.raises(ValueError):
         oracle.copy_blocks(kc, kc.copy(), [(0, 1), (1, 2)])     # destination is a source
+
+
+def test_fp8_store_changes_only_the_slots_and_rounds_to_nearest():
+    """Quantized store: only the target slots change, and each stored code is
+    a nearest E4M3 value of x / scale (within half a code step of it)."""
+    from oracle import decode_e4m3, reshape_and_cache_fp8
+    from synthetic import to_storage
+    rng = np.random.default_rng(4)
+    N, Hkv, B, D, T = 12, 3, 8, 16, 20
+    kc = rng.integers(0, 256, size=(N, Hkv, B, D)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(N, Hkv, B, D)).astype(np.uint8)
+    k = to_storage(rng.standard_normal((T, Hkv, D)) * 3, "bf16")
+    v = to_storage(rng.standard_normal((T, Hkv, D)) * 3, "bf16")
+    slots = rng.choice(N * B, size=T, replace=False).astype(np.int32)
+    slots[[2, 7]] = -1
+    k2, v2 = kc.copy(), vc.copy()
+    reshape_and_cache_fp8(k, v, k2, v2, slots, B, 0.05, 0.02, "bf16")
+    touched = np.zeros((N, B), dtype=bool)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        touched[s // B, s % B] = True
+        x = oracle.decode(k[i], "bf16").astype(np.float32) / np.float32(0.05)
+        got = decode_e4m3(k2[s // B, :, s % B, :])
+        step = np.where(np.abs(got) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -6))) - 3))
+        assert np.all(np.abs(got - x) <= step / 2 + 1e-12)
+    untouched = ~np.broadcast_to(touched[:, None, :, None], kc.shape)
+    assert np.array_equal(k2[untouched], kc[untouched])
+    assert np.array_equal(v2[untouched], vc[untouched])
