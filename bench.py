@@ -50,6 +50,7 @@ LENGTH_DESC = {
     4: "uniform [1024, 32768]",
     5: "1000-token shared prompt + uniform [1, 512] per-sample tail",
     6: "uniform [1024, 16384], attention over the last 4096",
+    8: "uniform [128, 2048]",
 }
 
 
@@ -70,7 +71,8 @@ def _oracle_rows(s):
     cfg = c["cfg"]
     oracle.paged_attention_decode(c["q"][s:s + 1], c["k"], c["v"], c["tables"][s:s + 1], c["lens"][s:s + 1],
                                   cfg.scale, cfg.block_size, cfg.num_kv_heads, cfg.dtype,
-                                  sliding_window=cfg.sliding_window)
+                                  sliding_window=cfg.sliding_window, kv_format=cfg.kv_format,
+                                  k_scale=cfg.k_scale, v_scale=cfg.v_scale)
     return s
 
 
@@ -117,7 +119,7 @@ def cpu_baseline(cfg, layout, cpu_seconds: float):
             elapsed = time.perf_counter() - t0
             if elapsed >= cpu_seconds:
                 break
-    nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.dtype, cfg.sliding_window) * reps
+    nbytes = kv_bytes(lens, cfg.num_kv_heads, cfg.head_dim, cfg.kv_dtype, cfg.sliding_window) * reps
     return {
         "value": round(nbytes / elapsed / 1e9, 4),
         "unit": "GB/s",
@@ -447,7 +449,7 @@ def main():
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
     S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     es = DTYPE_BYTES[cfg.dtype]
-    step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.dtype, cfg.sliding_window)
+    step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.kv_dtype, cfg.sliding_window)
     log(f"workload {cfg.name}: S={S} Hq={Hq} Hkv={Hkv} D={D} B={B} {cfg.dtype} sum(L)={int(layout.context_lens.sum())} "
         f"pool={layout.num_blocks} blocks KV/step={step_kv / 1e9:.3f} GB")
 
@@ -459,7 +461,7 @@ def main():
 
     import torch
     import paged_kv_cache_339_amd as pkv
-    from paged_kv_cache_339_amd._lib import KERNELS, AttnOptions, lib
+    from paged_kv_cache_339_amd._lib import KERNELS, KV_FORMATS, AttnOptions, lib
     from paged_kv_cache_339_amd.ops import dtype_code
     from synthetic import device_values
 
@@ -482,7 +484,8 @@ def main():
     out = torch.empty_like(q)
     code = dtype_code(q)
     max_ctx = layout.max_context_len
-    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, cfg.sliding_window)
+    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, cfg.sliding_window,
+                                   cfg.kv_format, cfg.k_scale, cfg.v_scale)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
@@ -492,7 +495,7 @@ def main():
     copy_args = None
     if pairs is not None:
         copy_args = (vp(kc.data_ptr()), vp(vc.data_ptr()), vp(pairs.data_ptr()), n_pairs, Hkv, B, D,
-                     layout.num_blocks, code, vp(stream))
+                     layout.num_blocks, dtype_code(kc), vp(stream))
 
     def step_args(opts):
         """pkv_decode_step: store each sequence's new token and attend."""
@@ -505,8 +508,10 @@ def main():
     begins = [ev.create() for _ in range(K)]
     ends = [ev.create() for _ in range(K)]
     win = cfg.sliding_window
-    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win)
-    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win) for i in range(K)]
+    kvf = KV_FORMATS[cfg.kv_format]
+    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale)
+    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win, kvf, cfg.k_scale, cfg.v_scale)
+             for i in range(K)]
     warm_args = step_args(plain)
     timed_args = [step_args(o) for o in timed]
 
@@ -547,7 +552,7 @@ def main():
     lens64 = layout.context_lens.astype(np.int64)
     first = np.maximum(0, lens64 - win) // B if win > 0 else np.zeros_like(lens64)
     nblk = -(-lens64 // B) - first                    # table entries read per (sequence, KV head)
-    alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4
+    alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4   # es: q / out format
     achieved = alg_bytes / main_s / 1e9
     kv_gbps = step_kv / step_s / 1e9
     kernel_used = args.kernel if args.kernel != "auto" else (
@@ -568,10 +573,10 @@ def main():
         "config": {
             "workload": cfg.name,
             "batch": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B,
-            "kv_dtype": cfg.dtype, "context_lens": LENGTH_DESC[args.config],
+            "kv_dtype": cfg.kv_dtype, "context_lens": LENGTH_DESC[args.config],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
             "kv_bytes_per_step": step_kv, "partition_size": part, "kernel": kernel_used,
-            "sliding_window": win,
+            "sliding_window": win, "kv_format": cfg.kv_format,
             "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
         },
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),

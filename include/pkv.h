@@ -46,7 +46,16 @@
 extern "C" {
 #endif
 
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* Element formats.  PKV_FP8_E4M3 (OCP 8-bit E4M3, finite: bias 7, no
+ * infinities, S.1111.111 = NaN, largest magnitude 448) is a KV-cache format
+ * only: queries and outputs stay f32/f16/bf16. */
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
+
+/* KV-cache format of the attention calls (pkv_attn_options.kv_format). */
+enum pkv_kv_format {
+  PKV_KV_SAME = 0,       /* caches hold the query's format */
+  PKV_KV_FP8_E4M3 = 1    /* caches hold E4M3 codes; value = e4m3(code) * k_scale (v_scale) */
+};
 
 enum pkv_status {
   PKV_OK = 0,
@@ -102,6 +111,15 @@ typedef struct pkv_attn_options {
    * Table entries of blocks wholly before the window are never read (they
    * may be -1 once pkv_bm_slide_window released them). */
   int32_t sliding_window;
+  /* Cache format (enum pkv_kv_format) and, for PKV_KV_FP8_E4M3, the
+   * per-tensor scales: a stored code c stands for e4m3(c) * k_scale in the
+   * key cache and e4m3(c) * v_scale in the value cache ("pagedattention
+   * vllm" glossary, Comparison with Alternatives > vs Compression: paging
+   * combined with quantization).  Scales must be finite and > 0; they are
+   * ignored for PKV_KV_SAME. */
+  int32_t kv_format;
+  float k_scale;
+  float v_scale;
 } pkv_attn_options;
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes and
@@ -187,7 +205,9 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
 
 /*
  * Store each new token's key and value into the block slot the block
- * manager reserved for it ("What is PagedAttention" (tecyfy), How it works:
+ * manager reserved for it, in the caches' own format (f32/f16/bf16; for
+ * 8-bit caches see pkv_reshape_and_cache_fp8) ("What is PagedAttention"
+ * (tecyfy), How it works:
  * blocks handed out as the sequence grows):
  *   k_cache[slot / B][h][slot % B][:] = k[i][h][:]   (and v), all h,
  * for every i with 0 <= slot = slot_mapping[i] < num_blocks * B.  Negative
@@ -200,6 +220,19 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
                           pkv_dtype dtype, void* stream);
+
+/*
+ * reshape_and_cache into 8-bit caches: every value x of the new token's key
+ * (value) row, in format in_dtype (f32/f16/bf16), is stored as the E4M3 code
+ * of fp32(x) / k_scale (v_scale): fp32 division, round to nearest with ties
+ * to the even code, saturating at +-448 (448 itself included), NaN stored as
+ * 0x7F.  Caches: uint8 [num_blocks, num_kv_heads, block_size, head_dim].
+ * Slots as in pkv_reshape_and_cache.  k_scale, v_scale finite and > 0.
+ */
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              pkv_dtype in_dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * Copy-on-write block copies ("pagedattention vllm" glossary, Copy-on-Write

@@ -21,10 +21,11 @@ from .ops import (
     gather_kv,
     paged_attention_decode,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     workspace_bytes,
 )
 
 __all__ = [
     "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
-    "paged_attention_decode", "reshape_and_cache", "workspace_bytes",
+    "paged_attention_decode", "reshape_and_cache", "reshape_and_cache_fp8", "workspace_bytes",
 ]

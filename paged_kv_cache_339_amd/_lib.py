@@ -6,7 +6,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+KV_FORMATS = {"same": 0, "fp8_e4m3": 1}
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 
 c_i32, c_f32, c_size, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -15,7 +16,8 @@ c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 class AttnOptions(ctypes.Structure):
     _fields_ = [("partition_size", c_i32), ("kernel", c_i32),
-                ("main_begin_event", c_vp), ("main_end_event", c_vp), ("sliding_window", c_i32)]
+                ("main_begin_event", c_vp), ("main_end_event", c_vp), ("sliding_window", c_i32),
+                ("kv_format", c_i32), ("k_scale", c_f32), ("v_scale", c_f32)]
 
 
 class PkvError(RuntimeError):
@@ -51,6 +53,8 @@ def load(path: str = LIB_PATH):
                                                                               ctypes.POINTER(AttnOptions), c_vp]),
         "pkv_reshape_and_cache": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                                  c_i32, ctypes.c_int, c_vp]),
+        "pkv_reshape_and_cache_fp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                                     c_i32, ctypes.c_int, c_f32, c_f32, c_vp]),
         "pkv_copy_blocks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                            c_vp]),
         "pkv_gather_kv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,

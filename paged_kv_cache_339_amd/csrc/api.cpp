@@ -31,9 +31,12 @@ int dtype_bytes(pkv_dtype dt) {
     case PKV_F32: return 4;
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
     default: return 0;
   }
 }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -42,6 +45,7 @@ bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 // Workspace layout: [work header][work pairs][partition outputs][partition (m, l)].
 struct Plan {
   int kernel;
+  bool fp8;
   int32_t window;
   int32_t part_blocks;
   int32_t max_parts;
@@ -57,9 +61,16 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
               int32_t block_size, int32_t max_context_len, pkv_dtype dtype,
               const pkv_attn_options* opts, Plan* plan) {
-  if (dtype_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (dtype_bytes(dtype) == 0 || dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
     return PKV_ERR_SHAPE;
+  const int32_t kv_format = opts ? opts->kv_format : PKV_KV_SAME;
+  if (kv_format != PKV_KV_SAME && kv_format != PKV_KV_FP8_E4M3) return PKV_ERR_DTYPE;
+  const bool fp8 = kv_format == PKV_KV_FP8_E4M3;
+  if (fp8) {
+    if (dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
+    if (!good_scale(opts->k_scale) || !good_scale(opts->v_scale)) return PKV_ERR_SHAPE;
+  }
   if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
@@ -68,8 +79,10 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   const bool mfma_group = group == 4 || group == 8 || group == 16;
   const bool valu_group = group == 1 || group == 2 || group == 4 || group == 8;
   int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
-  if (kernel == PKV_KERNEL_AUTO) kernel = (sixteen_bit && mfma_group) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
-  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group)) return PKV_ERR_UNSUPPORTED;
+  if (kernel == PKV_KERNEL_AUTO)
+    kernel = (sixteen_bit && mfma_group && !fp8) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
+  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group && !fp8)) return PKV_ERR_UNSUPPORTED;
+  if (fp8 && (block_size == 8 || block_size == 64)) return PKV_ERR_UNSUPPORTED;
   if (kernel == PKV_KERNEL_VALU && !valu_group) return PKV_ERR_UNSUPPORTED;
   if (kernel != PKV_KERNEL_MFMA && kernel != PKV_KERNEL_VALU) return PKV_ERR_SHAPE;
 
@@ -109,6 +122,7 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
     plan->max_parts = (int32_t)((span_blocks + plan->part_blocks - 1) / plan->part_blocks);
   }
   plan->window = window;
+  plan->fp8 = fp8;
   if ((int64_t)num_seqs * num_kv_heads * plan->max_parts > kMaxGrid) return PKV_ERR_SHAPE;
   plan->kernel = kernel;
   plan->max_pairs = (int64_t)num_seqs * plan->max_parts;
@@ -209,7 +223,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.pairs = reinterpret_cast<pkv::WorkPair*>(ws + plan.pairs_off);
   p.ws_o = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_off) : nullptr;
   p.ws_ml = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_ml_off) : nullptr;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634 * (plan.fp8 ? (double)opts->k_scale : 1.0));
+  p.v_scale = plan.fp8 ? opts->v_scale : 1.f;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -233,7 +248,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   }
   const bool have = plan.kernel == PKV_KERNEL_MFMA
                         ? pkv::launch_attention_mfma(p, dtype, head_dim, block_size, group, s, &err)
-                        : pkv::launch_attention_valu(p, dtype, head_dim, block_size, group, s, &err);
+                        : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
+                                                     head_dim, block_size, group, s, &err);
   if (!have) return PKV_ERR_UNSUPPORTED;
   if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_end_event) {
@@ -279,14 +295,20 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
     if (!k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ALIGN;
   }
+  const bool fp8 = opts && opts->kv_format == PKV_KV_FP8_E4M3;
   pkv::AppendArgs a;
   a.k = static_cast<const char*>(k_new);
   a.v = static_cast<const char*>(v_new);
   a.k_cache = static_cast<char*>(k_cache);
   a.v_cache = static_cast<char*>(v_cache);
   a.slot_mapping = slot_mapping;
-  a.chunks = head_dim * es / 16;
+  a.chunks = fp8 ? head_dim / 16 : head_dim * es / 16;
   a.num_slots = (int64_t)num_blocks * block_size;
+  a.fp8 = fp8 ? 1 : 0;
+  a.in_dtype = dtype;
+  a.head_dim = head_dim;
+  a.k_scale = fp8 ? opts->k_scale : 1.f;
+  a.v_scale = fp8 ? opts->v_scale : 1.f;
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                      num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                      max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts, stream, &a);
@@ -310,6 +332,27 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
   return launch_status(pkv::launch_reshape_and_cache(
       k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim * es, block_size,
       num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              pkv_dtype in_dtype, float k_scale, float v_scale, void* stream) {
+  const int es = dtype_bytes(in_dtype);
+  if (!es || in_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (!good_scale(k_scale) || !good_scale(v_scale)) return PKV_ERR_SHAPE;
+  if (head_dim % 16) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_heads * head_dim / 16 > 0x7fffffff / 64) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGN;
+  clear_pending_error();
+  return launch_status(pkv::launch_reshape_and_cache_fp8(
+      k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+      num_blocks, in_dtype, k_scale, v_scale, static_cast<hipStream_t>(stream)));
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, int32_t num_pairs,

@@ -106,7 +106,7 @@ __device__ __forceinline__ void merge_and_store(const AttnParams& p, const Merge
       tot = fmaf(sm.l[w][g], a, tot);
       o = fmaf(sm.o[w][g][d], a, o);
     }
-    const float r = bad ? __builtin_nanf("") : o / tot;
+    const float r = bad ? __builtin_nanf("") : o / tot * p.v_scale;
     const int hq = h * G + g;
     if (nparts == 1) {
       store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + hq) * D + d, r);

@@ -157,8 +157,17 @@ __global__ __launch_bounds__(kWave) void append_and_plan_kernel(AttnParams p, in
     plan_body(p, B);
     return;
   }
-  scatter_token(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, blockIdx.x - 1, p.num_kv_heads,
-                a.chunks, B, a.num_slots);
+  const int i = blockIdx.x - 1;
+  if (!a.fp8) {
+    scatter_token(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads, a.chunks, B,
+                  a.num_slots);
+  } else if (a.in_dtype == PKV_F16) {
+    scatter_token_fp8<PKV_F16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads,
+                               a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
+  } else if (a.in_dtype == PKV_BF16) {
+    scatter_token_fp8<PKV_BF16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads,
+                                a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
+  }
 }
 
 hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,

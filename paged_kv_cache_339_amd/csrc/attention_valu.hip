@@ -19,9 +19,11 @@
 
 namespace pkv {
 
-template <int DT, int D, int B, int G, int NW, int U>
+// DT: query / output format; KT: cache format (DT, or 8-bit E4M3 codes).
+template <int DT, int KT, int D, int B, int G, int NW, int U>
 __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
-  constexpr int ES = Format<DT>::kBytes;
+  constexpr int ES = Format<KT>::kBytes;
+  constexpr int QES = Format<DT>::kBytes;
   constexpr int EPL = 16 / ES;       // elements per lane per load
   constexpr int LPT = D / EPL;       // lanes per token row
   constexpr int TPW = kWave / LPT;   // token rows per wave-wide load
@@ -60,8 +62,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * ES;
-    widen16<DT>(load16(qrow), qf[g]);
+                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * QES;
+#pragma unroll
+    for (int l = 0; l < EPL * QES / 16; ++l) widen16<DT>(load16(qrow + 16 * l), qf[g] + l * (16 / QES));
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
   }
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           float kf[EPL];
-          widen16<DT>(kr[u][i], kf);
+          widen16<KT>(kr[u][i], kf);
           const int row = i * TPW + grp;
           const bool row_ok = row >= first[u] && row < valid[u];
 #pragma unroll
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           float vf[EPL];
-          widen16<DT>(vr[u][i], vf);
+          widen16<KT>(vr[u][i], vf);
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -221,59 +224,73 @@ namespace {
 constexpr int kValuWaves = PKV_VALU_WAVES;
 
 // Blocks a wave loads ahead: two tiles of 8 fp32 rows of 128 already make
-// 64 KiB of registers per wave in flight, so f32 and wide groups take one.
-template <int DT, int D, int G>
+// 64 KiB of registers per wave in flight, so f32 and wide groups take one;
+// 8-bit tiles are half the bytes of 16-bit ones, so they take twice as many.
+template <int DT, int KT, int D, int G>
 constexpr int valu_unroll() {
+  if constexpr (KT == PKV_FP8_E4M3) return G <= 2 ? 2 * PKV_VALU_UNROLL : 1;
   return (DT == PKV_F32 && D == 128) || G >= 4 ? 1 : PKV_VALU_UNROLL;
 }
 
-template <int DT, int D, int B, int G>
+template <int DT, int KT, int D, int B, int G>
 hipError_t launch_valu(const AttnParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
-  hipLaunchKernelGGL((attn_valu_kernel<DT, D, B, G, kValuWaves, valu_unroll<DT, D, G>()>), grid,
+  hipLaunchKernelGGL((attn_valu_kernel<DT, KT, D, B, G, kValuWaves, valu_unroll<DT, KT, D, G>()>), grid,
                      dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
   return hipGetLastError();
 }
 
-template <int DT, int D, int B>
+template <int DT, int KT, int D, int B>
 bool by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
   switch (G) {
-    case 1: *e = launch_valu<DT, D, B, 1>(p, st); return true;
-    case 2: *e = launch_valu<DT, D, B, 2>(p, st); return true;
-    case 4: *e = launch_valu<DT, D, B, 4>(p, st); return true;
-    case 8: *e = launch_valu<DT, D, B, 8>(p, st); return true;
+    case 1: *e = launch_valu<DT, KT, D, B, 1>(p, st); return true;
+    case 2: *e = launch_valu<DT, KT, D, B, 2>(p, st); return true;
+    case 4: *e = launch_valu<DT, KT, D, B, 4>(p, st); return true;
+    case 8: *e = launch_valu<DT, KT, D, B, 8>(p, st); return true;
     default: return false;
   }
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 bool by_block(const AttnParams& p, int B, int G, hipStream_t st, hipError_t* e) {
   switch (B) {
-    case 8: return by_group<DT, D, 8>(p, G, st, e);
-    case 16: return by_group<DT, D, 16>(p, G, st, e);
-    case 32: return by_group<DT, D, 32>(p, G, st, e);
-    case 64: return by_group<DT, D, 64>(p, G, st, e);
+    case 8:
+      if constexpr (KT != PKV_FP8_E4M3) return by_group<DT, KT, D, 8>(p, G, st, e);
+      return false;
+    case 16: return by_group<DT, KT, D, 16>(p, G, st, e);
+    case 32: return by_group<DT, KT, D, 32>(p, G, st, e);
+    case 64:
+      if constexpr (KT != PKV_FP8_E4M3) return by_group<DT, KT, D, 64>(p, G, st, e);
+      return false;
     default: return false;
   }
 }
 
-template <int DT>
+template <int DT, int KT>
 bool by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipError_t* e) {
   switch (D) {
-    case 64: return by_block<DT, 64>(p, B, G, st, e);
-    case 128: return by_block<DT, 128>(p, B, G, st, e);
+    case 64: return by_block<DT, KT, 64>(p, B, G, st, e);
+    case 128: return by_block<DT, KT, 128>(p, B, G, st, e);
     default: return false;
   }
 }
 
 }  // namespace
 
-bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
-                           int group, hipStream_t stream, hipError_t* err) {
+bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                           int block_size, int group, hipStream_t stream, hipError_t* err) {
+  if (kv == PKV_FP8_E4M3) {
+    switch (dt) {
+      case PKV_F16: return by_dim<PKV_F16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err);
+      case PKV_BF16: return by_dim<PKV_BF16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err);
+      default: return false;
+    }
+  }
+  if (kv != dt) return false;
   switch (dt) {
-    case PKV_F32: return by_dim<PKV_F32>(p, head_dim, block_size, group, stream, err);
-    case PKV_F16: return by_dim<PKV_F16>(p, head_dim, block_size, group, stream, err);
-    case PKV_BF16: return by_dim<PKV_BF16>(p, head_dim, block_size, group, stream, err);
+    case PKV_F32: return by_dim<PKV_F32, PKV_F32>(p, head_dim, block_size, group, stream, err);
+    case PKV_F16: return by_dim<PKV_F16, PKV_F16>(p, head_dim, block_size, group, stream, err);
+    case PKV_BF16: return by_dim<PKV_BF16, PKV_BF16>(p, head_dim, block_size, group, stream, err);
     default: return false;
   }
 }

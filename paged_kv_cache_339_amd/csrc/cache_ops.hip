@@ -32,6 +32,50 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
   return hipGetLastError();
 }
 
+// Quantizing store into 8-bit caches, one workgroup per new token.
+template <int IT>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int64_t num_slots, float k_scale, float v_scale) {
+  scatter_token_fp8<IT>(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, num_kv_heads, head_dim,
+                        block_size, num_slots, k_scale, v_scale);
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                        const int32_t* slot_mapping, int32_t num_tokens,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, pkv_dtype in_dtype, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int per_tok = num_kv_heads * (head_dim / 16);
+  const int threads = per_tok >= 256 ? 256 : (per_tok + 63) / 64 * 64;
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  const char* kk = static_cast<const char*>(k);
+  const char* vv = static_cast<const char*>(v);
+  char* kc = static_cast<char*>(k_cache);
+  char* vc = static_cast<char*>(v_cache);
+  switch (in_dtype) {
+    case PKV_F32:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_F32>, dim3((unsigned)num_tokens), dim3(threads), 0,
+                         stream, kk, vv, kc, vc, slot_mapping, num_kv_heads, head_dim, block_size, slots,
+                         k_scale, v_scale);
+      break;
+    case PKV_F16:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_F16>, dim3((unsigned)num_tokens), dim3(threads), 0,
+                         stream, kk, vv, kc, vc, slot_mapping, num_kv_heads, head_dim, block_size, slots,
+                         k_scale, v_scale);
+      break;
+    case PKV_BF16:
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<PKV_BF16>, dim3((unsigned)num_tokens), dim3(threads), 0,
+                         stream, kk, vv, kc, vc, slot_mapping, num_kv_heads, head_dim, block_size, slots,
+                         k_scale, v_scale);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Each workgroup copies one 16 KiB piece of one block of one cache.
 constexpr int kCopyPiece = 16384;
 

@@ -16,6 +16,7 @@ template <int DT> struct Format;
 template <> struct Format<PKV_F32>  { static constexpr int kBytes = 4; };
 template <> struct Format<PKV_F16>  { static constexpr int kBytes = 2; };
 template <> struct Format<PKV_BF16> { static constexpr int kBytes = 2; };
+template <> struct Format<PKV_FP8_E4M3> { static constexpr int kBytes = 1; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -54,10 +55,24 @@ __device__ __forceinline__ float widen_half<PKV_BF16>(uint32_t w, bool hi) {
   return __builtin_bit_cast(float, hi ? (w & 0xffff0000u) : (w << 16));
 }
 
-// 16 stored bytes -> 16/kBytes floats.
+// 16 stored bytes -> 16/kBytes floats.  E4M3 codes go through the
+// hardware conversion (v_cvt_pk_f32_fp8 decodes OCP E4M3 on gfx950, NaN
+// codes included; checked against the format definition on all 256 codes).
 template <int DT>
 __device__ __forceinline__ void widen16(const u32x4& raw, float* f) {
-  if constexpr (DT == PKV_F32) {
+  if constexpr (DT == PKV_FP8_E4M3) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int w = (int)raw[i];
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  } else if constexpr (DT == PKV_F32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // Copy the element out first: a bit_cast applied directly to an

@@ -33,7 +33,8 @@ struct AttnParams {
   float* ws_ml;               // [S, Hq, P, 2]  (running max in log2 units, sum)
   WorkHeader* work;           // plan written by the plan kernel
   WorkPair* pairs;            // [max_pairs]
-  float scale_log2;           // scale * log2(e)
+  float scale_log2;           // scale * log2(e), times k_scale for 8-bit caches
+  float v_scale;              // 1, or the value-cache scale of 8-bit caches
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -47,8 +48,9 @@ struct AttnParams {
 };
 
 // Returns false when no kernel instance exists for the combination.
-bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
-                           int group, hipStream_t stream, hipError_t* err);
+// dt: the query / output format; kv: the caches' (dt, or PKV_FP8_E4M3).
+bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                           int block_size, int group, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                            int group, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
@@ -61,14 +63,23 @@ struct AppendArgs {
   char* k_cache;
   char* v_cache;
   const int32_t* slot_mapping;  // [num_seqs]
-  int32_t chunks;             // 16-byte pieces per (token, head) row
+  int32_t chunks;             // 16-byte pieces per (token, head) row of the cache
   int64_t num_slots;          // num_blocks * block_size
+  int32_t fp8;                // store E4M3 codes of x / scale (in_dtype rows)
+  int32_t in_dtype;           // format of k, v when fp8
+  int32_t head_dim;
+  float k_scale, v_scale;
 };
 hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,
                                   hipStream_t stream);
 bool launch_attention_reduce(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                              hipStream_t stream, hipError_t* err);
 
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                                        const int32_t* slot_mapping, int32_t num_tokens,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, pkv_dtype in_dtype, float k_scale,
+                                        float v_scale, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,

@@ -10,7 +10,7 @@ import ctypes
 
 import numpy as np
 
-from ._lib import KERNELS, AttnOptions, PkvError, c_i32p, check, lib
+from ._lib import KERNELS, KV_FORMATS, AttnOptions, PkvError, c_i32p, check, lib
 
 
 def _torch():
@@ -19,8 +19,9 @@ def _torch():
 
 
 def dtype_code(t) -> int:
+    """Element format of a tensor: 8-bit caches are uint8 (or float8_e4m3fn) tensors of E4M3 codes."""
     torch = _torch()
-    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.uint8: 3, torch.float8_e4m3fn: 3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -48,28 +49,35 @@ def _dev(t, name, dtype=None, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _options(partition_size, kernel, main_events, sliding_window=0):
+def _options(partition_size, kernel, main_events, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
     ev0, ev1 = (None, None) if main_events is None else main_events
     return AttnOptions(int(partition_size), KERNELS[kernel],
                        None if ev0 is None else ctypes.c_void_p(int(ev0)),
-                       None if ev1 is None else ctypes.c_void_p(int(ev1)), int(sliding_window))
+                       None if ev1 is None else ctypes.c_void_p(int(ev1)), int(sliding_window),
+                       KV_FORMATS[kv_format], float(k_scale), float(v_scale))
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                    dtype_code_, partition_size=0, kernel="auto", sliding_window=0) -> int:
-    opts = _options(partition_size, kernel, None, sliding_window)
+                    dtype_code_, partition_size=0, kernel="auto", sliding_window=0, kv_format="same",
+                    k_scale=1.0, v_scale=1.0) -> int:
+    opts = _options(partition_size, kernel, None, sliding_window, kv_format, k_scale, v_scale)
     return int(lib.pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        block_size, max_context_len, dtype_code_,
                                                        ctypes.byref(opts)))
 
 
-def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads):
+def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                            kv_format="same"):
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
     if tuple(out.shape) != (S, Hq, D) or out.dtype != q.dtype:
         raise ValueError("out must match q")
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("k_cache and v_cache must match each other and q's dtype")
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match each other")
+    if kv_format == "same" and k_cache.dtype != q.dtype:
+        raise ValueError("the caches must have q's dtype")
+    if kv_format == "fp8_e4m3" and dtype_code(k_cache) != 3:
+        raise ValueError("8-bit caches must be uint8 (or float8_e4m3fn) tensors of E4M3 codes")
     if D2 != D or B != block_size or Hkv != num_kv_heads:
         raise ValueError("cache shape disagrees with head_dim / block_size / num_kv_heads")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
@@ -77,8 +85,9 @@ def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens
 
 
 def _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, device,
-               sliding_window=0):
-    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, sliding_window)
+               sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
+    need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, sliding_window,
+                           kv_format, k_scale, v_scale)
     if need and workspace is None:
         workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
     return workspace
@@ -92,7 +101,8 @@ def _ws_args(workspace):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, max_context_len, partition_size=0, kernel="auto",
-                           workspace=None, stream=None, main_events=None, sliding_window=0):
+                           workspace=None, stream=None, main_events=None, sliding_window=0, kv_format="same",
+                           k_scale=1.0, v_scale=1.0):
     """out[s, j] = softmax(scale * q[s, j] K_s^T) V_s through the block tables.
 
     q, out: [S, Hq, D]; k_cache, v_cache: [N, Hkv, B, D]; block_tables int32
@@ -102,11 +112,12 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     torch = _torch()
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
-    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads)
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                            kv_format)
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
-                           sliding_window)
-    opts = _options(partition_size, kernel, main_events, sliding_window)
+                           sliding_window, kv_format, k_scale, v_scale)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale)
     st = lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
@@ -118,14 +129,15 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
 def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
                 block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
-                stream=None, main_events=None, sliding_window=0):
+                stream=None, main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
     """reshape_and_cache(k_new, v_new, ..., slot_mapping) followed by
     paged_attention_decode(...), with the token store and the attention work
     list in one launch.  k_new, v_new: [S, Hkv, D]; slot_mapping int32 [S]."""
     torch = _torch()
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
-    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads)
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                            kv_format)
     if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
         raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
     if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
@@ -134,8 +146,8 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
         raise ValueError("slot_mapping must be [num_seqs]")
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
-                           sliding_window)
-    opts = _options(partition_size, kernel, main_events, sliding_window)
+                           sliding_window, kv_format, k_scale, v_scale)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale)
     st = lib.pkv_decode_step(
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),
@@ -144,6 +156,24 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
         *_ws_args(workspace), ctypes.byref(opts), _stream(stream))
     check(st, "decode_step")
     return out
+
+
+def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=None):
+    """k_cache[slot // B, :, slot % B] = E4M3 code of k[i] / k_scale (and v), for every slot >= 0.
+    k, v: f32/f16/bf16 [T, Hkv, D]; caches uint8 [N, Hkv, B, D]."""
+    torch = _torch()
+    T, Hkv, D = k.shape
+    N, Hkv2, B, D2 = k_cache.shape
+    if tuple(v.shape) != (T, Hkv, D) or (Hkv2, D2) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between new tokens and caches")
+    if dtype_code(k_cache) != 3 or dtype_code(v_cache) != 3 or k.dtype != v.dtype:
+        raise TypeError("caches must hold E4M3 codes and k, v share a dtype")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = lib.pkv_reshape_and_cache_fp8(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                       _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, B, N,
+                                       dtype_code(k), float(k_scale), float(v_scale), _stream(stream))
+    check(st, "reshape_and_cache_fp8")
 
 
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, stream=None):

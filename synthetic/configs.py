@@ -14,7 +14,7 @@ from __future__ import annotations
 from dataclasses import dataclass, replace
 import math
 
-DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
 @dataclass(frozen=True)
@@ -38,6 +38,9 @@ class DecodeConfig:
     prompt_len: int = 0      # shared-prefix workloads only
     samples_per_prompt: int = 0
     sliding_window: int = 0  # attend to the last W tokens; blocks wholly before them are released
+    kv_format: str = "same"  # "same" (caches in `dtype`) or "fp8_e4m3" (8-bit codes with scales)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:
@@ -50,6 +53,11 @@ class DecodeConfig:
     @property
     def dtype_bytes(self) -> int:
         return DTYPE_BYTES[self.dtype]
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage format of the caches: `dtype`, or "fp8" (E4M3 codes)."""
+        return "fp8" if self.kv_format == "fp8_e4m3" else self.dtype
 
     def scaled(self, **kw) -> "DecodeConfig":
         return replace(self, **kw)
@@ -79,6 +87,11 @@ CONFIGS = {
     # A sliding-window grouped-query layer (Mistral-7B-like: 32 query heads
     # over 8 KV heads, 4096-token window): only the blocks the window touches
     # hold data; table entries before them are -1.
+    # The Llama-2-7B-shaped layer with an 8-bit E4M3 KV cache (per-tensor
+    # scales 1/32; paging combined with quantization).
+    8: DecodeConfig("llama2_7b_layer_fp8kv", num_seqs=64, num_q_heads=32, num_kv_heads=32,
+                    head_dim=128, dtype="f16", block_size=16, lengths="uniform",
+                    len_lo=128, len_hi=2048, kv_format="fp8_e4m3", k_scale=1.0 / 32, v_scale=1.0 / 32),
     6: DecodeConfig("swa_mistral7b_layer_bf16", num_seqs=64, num_q_heads=32, num_kv_heads=8,
                     head_dim=128, dtype="bf16", block_size=16, lengths="uniform",
                     len_lo=1024, len_hi=16384, sliding_window=4096),

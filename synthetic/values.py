@@ -5,6 +5,7 @@ Storage conventions shared by every consumer:
   f32  -> numpy float32 / torch.float32
   f16  -> numpy float16 / torch.float16
   bf16 -> numpy uint16 bit patterns / torch.bfloat16
+  fp8  -> numpy uint8 E4M3 codes / torch.uint8 (8-bit caches only)
 
 Pool slots that hold no token before the step are poisoned with all-ones bit
 patterns (a NaN in every format), so a read of a slot outside a sequence shows
@@ -19,8 +20,9 @@ import numpy as np
 
 from .layout import Layout
 
-_NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-POISON_BITS = {"f32": 0xFFFFFFFF, "f16": 0xFFFF, "bf16": 0xFFFF}
+_NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
+POISON_BITS = {"f32": 0xFFFFFFFF, "f16": 0xFFFF, "bf16": 0xFFFF, "fp8": 0xFF}
+_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
@@ -37,8 +39,18 @@ def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _poison(shape, dtype):
-    bits = np.full(shape, POISON_BITS[dtype], dtype=np.uint32 if dtype == "f32" else np.uint16)
+    bits = np.full(shape, POISON_BITS[dtype], dtype=_BITS[dtype])
     return bits.view(_NP_STORAGE[dtype])
+
+
+def e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Random finite E4M3 codes for an 8-bit cache: random sign, exponent
+    field uniform in 1..12 (magnitudes 2^-6 .. 60, a wide dynamic range),
+    mantissa uniform.  Integers only: nothing is rounded."""
+    sign = rng.integers(0, 2, size=shape).astype(np.uint8) << 7
+    exp = rng.integers(1, 13, size=shape).astype(np.uint8) << 3
+    man = rng.integers(0, 8, size=shape).astype(np.uint8)
+    return (sign | exp | man).astype(np.uint8)
 
 
 @dataclass
@@ -60,10 +72,14 @@ def host_values(layout: Layout) -> HostStep:
     S = len(layout.context_lens)
     N, dt = layout.num_blocks, cfg.dtype
     q = to_storage(_normal(seed, 1, (S, Hq, D)), dt)
+    kvdt = cfg.kv_dtype
     caches = []
     for stream in (2, 3):
-        full = to_storage(_normal(seed, stream, (N, Hkv, B, D)), dt)
-        cache = _poison((N, Hkv, B, D), dt)
+        if kvdt == "fp8":
+            full = e4m3_codes(np.random.default_rng([seed, stream]), (N, Hkv, B, D))
+        else:
+            full = to_storage(_normal(seed, stream, (N, Hkv, B, D)), dt)
+        cache = _poison((N, Hkv, B, D), kvdt)
         blk, off = np.nonzero(layout.live)
         cache[blk, :, off, :] = full[blk, :, off, :]
         r = layout.cow_rows
@@ -107,9 +123,16 @@ def device_values(layout: Layout, device="cuda"):
     dead = torch.from_numpy(~layout.live).to(device)
     caches = []
     for stream in (2, 3):
-        cache = normal((N, Hkv, B, D), stream)
-        view = cache.view(torch.int16) if tdt != torch.float32 else cache.view(torch.int32)
-        view.masked_fill_(dead[:, None, :, None], -1)
+        if cfg.kv_dtype == "fp8":
+            g = gen(stream)
+            sign = torch.randint(0, 2, (N, Hkv, B, D), generator=g, device=device, dtype=torch.uint8) << 7
+            expo = torch.randint(1, 13, (N, Hkv, B, D), generator=g, device=device, dtype=torch.uint8) << 3
+            cache = sign | expo | torch.randint(0, 8, (N, Hkv, B, D), generator=g, device=device, dtype=torch.uint8)
+            cache.masked_fill_(dead[:, None, :, None], 0xFF)
+        else:
+            cache = normal((N, Hkv, B, D), stream)
+            view = cache.view(torch.int16) if tdt != torch.float32 else cache.view(torch.int32)
+            view.masked_fill_(dead[:, None, :, None], -1)
         if len(layout.cow_pairs):
             r = layout.cow_rows
             src = torch.from_numpy(layout.cow_pairs[:, 0].astype(np.int64)).to(device)

@@ -28,8 +28,8 @@ def run_case(cfg: DecodeConfig, seed: int, lengths=None, partition_size=0, kerne
     out = step.attend(partition_size=partition_size, kernel=kernel)
     torch.cuda.synchronize()
     want, kc, vc = oracle_step(lay, host)
-    assert to_storage_np(step.k_cache, cfg.dtype).tobytes() == kc.tobytes()
-    assert to_storage_np(step.v_cache, cfg.dtype).tobytes() == vc.tobytes()
+    assert to_storage_np(step.k_cache, cfg.kv_dtype).tobytes() == kc.tobytes()
+    assert to_storage_np(step.v_cache, cfg.kv_dtype).tobytes() == vc.tobytes()
     return assert_rows_close(widen(out), want, cfg.dtype, label or cfg.name)
 
 
@@ -39,6 +39,7 @@ def test_config1_every_row(partition_size):
 
 
 SCALED = {
+    8: dict(num_seqs=6),
     6: dict(num_seqs=6),
     2: dict(num_seqs=6),
     3: dict(num_seqs=24),
@@ -47,7 +48,7 @@ SCALED = {
 }
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8])
 def test_scaled_workloads_every_row(idx):
     cfg = CONFIGS[idx].scaled(**SCALED[idx])
     run_case(cfg, seed=10 + idx, partition_size=cfg.partition_size, label=f"config{idx}-scaled")
@@ -218,7 +219,7 @@ def test_work_list_covers_every_partition_longest_first():
     assert rest[-2:] == [0, 0], "empty sequences come last"
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 8])
 def test_decode_step_equals_scatter_then_attend(idx):
     """The fused step stores the same bytes and returns the same bits as
     reshape_and_cache followed by paged_attention_decode, and matches the
@@ -234,11 +235,13 @@ def test_decode_step_equals_scatter_then_attend(idx):
     out_b = torch.empty_like(b.q)
     pkv.decode_step(out_b, b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.slots, b.tables, b.lens, cfg.scale,
                     cfg.block_size, cfg.num_kv_heads, max(1, lay.max_context_len),
-                    partition_size=cfg.partition_size, sliding_window=cfg.sliding_window)
+                    partition_size=cfg.partition_size, sliding_window=cfg.sliding_window,
+                    kv_format=cfg.kv_format, k_scale=cfg.k_scale, v_scale=cfg.v_scale)
     torch.cuda.synchronize()
-    view = torch.int32 if cfg.dtype == "f32" else torch.int16
+    view = {"f32": torch.int32, "fp8": torch.uint8}.get(cfg.kv_dtype, torch.int16)
     assert torch.equal(a.k_cache.view(view), b.k_cache.view(view))
     assert torch.equal(a.v_cache.view(view), b.v_cache.view(view))
+    view = torch.int32 if cfg.dtype == "f32" else torch.int16
     assert torch.equal(out_a.view(view), out_b.view(view))
     want, _, _ = oracle_step(lay, host)
     assert_rows_close(widen(out_b), want, cfg.dtype, f"decode_step config {idx}")

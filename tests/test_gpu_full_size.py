@@ -13,7 +13,7 @@ import oracle
 import paged_kv_cache_339_amd as pkv
 from synthetic import CONFIGS, device_values, make_layout
 from tests.gpu_util import (DeviceStep, assert_rows_close, ints, oracle_on_snapshot, say,
-                            snapshot_sequences, widen)
+                            snapshot_sequences, to_storage_np, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def _sample(lay, k, rng):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8])
 def test_full_size_sampled_rows(idx):
     cfg = CONFIGS[idx]
     lay = make_layout(cfg, seed=idx)
@@ -53,12 +53,18 @@ def test_full_size_sampled_rows(idx):
     out = step.attend(partition_size=cfg.partition_size)
     torch.cuda.synchronize()
 
-    # Every appended token sits at its slot, bit for bit.
+    # Every appended token sits at its slot, bit for bit (the oracle's codes
+    # of it for 8-bit caches).
     B = cfg.block_size
     slots = torch.from_numpy(lay.new_slots.astype(np.int64)).cuda()
-    for cache, new in ((step.k_cache, step.k_new), (step.v_cache, step.v_new)):
-        rows = cache[slots // B, :, slots % B, :]
-        assert torch.equal(rows.contiguous().view(torch.int16), new.view(torch.int16)), "reshape_and_cache"
+    for cache, new, scale in ((step.k_cache, step.k_new, cfg.k_scale), (step.v_cache, step.v_new, cfg.v_scale)):
+        rows = cache[slots // B, :, slots % B, :].contiguous()
+        if cfg.kv_format == "fp8_e4m3":
+            want = oracle.quantize_e4m3(oracle.decode(to_storage_np(new, cfg.dtype), cfg.dtype).astype(np.float32)
+                                        / np.float32(scale))
+            assert rows.cpu().numpy().tobytes() == want.tobytes(), "reshape_and_cache_fp8"
+        else:
+            assert torch.equal(rows.view(torch.int16), new.view(torch.int16)), "reshape_and_cache"
 
     want = oracle_on_snapshot(snap, cfg)
     got = widen(out.index_select(0, torch.tensor(seqs, device="cuda")))
