@@ -414,6 +414,49 @@ def beam_bench(args):
     }), flush=True)
 
 
+def swap_bench(args):
+    """Swapping for preemption: a quarter of the workload's live blocks go
+    to a pinned host pool (swap out) and come back (swap in), each direction
+    one pkv_swap_blocks launch, timed with HIP events."""
+    import torch
+    import paged_kv_cache_339_amd as pkv
+    from synthetic import device_values
+
+    cfg = CONFIGS[args.config]
+    layout = make_layout(cfg, seed=args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, kc, vc, _, _ = device_values(layout, device=dev)
+    used = layout.pool_order[:layout.used_blocks]
+    n = max(1, len(used) // 4)
+    host_k = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    host_v = torch.empty_like(host_k, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([used[:n], np.arange(n)], axis=1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), used[:n]], axis=1).astype(np.int32)).to(dev)
+    block_bytes = kc[0].numel() * kc.element_size()
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for name, fn in (("out", lambda: pkv.swap_blocks(host_k, host_v, kc, vc, out_pairs)),
+                     ("in", lambda: pkv.swap_blocks(kc, vc, host_k, host_v, in_pairs))):
+        for _ in range(args.warmup):
+            fn()
+        a, b = ev.create(), ev.create()
+        ev.record(a, stream)
+        for _ in range(args.steps):
+            fn()
+        ev.record(b, stream)
+        ms = ev.ms(a, b) / args.steps
+        res[name] = {"ms": round(ms, 4), "GBps": round(2 * n * block_bytes / ms / 1e6, 2)}
+    ev.close()
+    print(json.dumps({"metric": "swap_blocks GB/s between HBM and pinned host memory, 1 GPU",
+                      "value": round((res["out"]["GBps"] + res["in"]["GBps"]) / 2, 2), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                      "data": "synthetic", "config": {"workload": cfg.name, "blocks": int(n),
+                                                      "bytes_per_direction": int(2 * n * block_bytes)},
+                      "swap_out": res["out"], "swap_in": res["in"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +469,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of the decode step, time pkv_swap_blocks of a quarter of the workload's "
+                         "blocks to a pinned host pool and back (PCIe-bound)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the decode step, run copy_blocks over a known number of bytes "
                          "(the reference reading for the HBM traffic counters)")
@@ -441,6 +487,9 @@ def main():
         return
     if args.config in BEAM_CONFIGS:
         beam_bench(args)
+        return
+    if args.swap:
+        swap_bench(args)
         return
 
     cfg = CONFIGS[args.config]

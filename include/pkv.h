@@ -248,6 +248,24 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, 
                     pkv_dtype dtype, void* stream);
 
 /*
+ * Swapping ("pagedattention vllm" glossary, Memory Management > Swapping):
+ * for every pair p, block dst = pairs[p][1] of the destination pools becomes
+ * a bitwise copy of block src = pairs[p][0] of the source pools (keys and
+ * values, all heads).  Either side may be device memory or pinned host
+ * memory the device can address at the same address (hipHostMalloc / torch
+ * pin_memory); any other pointer (pageable memory) is refused with
+ * PKV_ERR_UNSUPPORTED before anything runs.  Swap out is device -> host,
+ * swap in host -> device; the copy runs as one kernel, bounded by PCIe for
+ * host pools.  pairs: device int32
+ * [num_pairs, 2]; destinations distinct; pairs naming a block outside its
+ * pool are skipped.  Same element layout and sizes as the caches.
+ */
+int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                    const int32_t* src_dst_pairs, int32_t num_pairs, int32_t num_src_blocks,
+                    int32_t num_dst_blocks, int32_t num_kv_heads, int32_t block_size,
+                    int32_t head_dim, pkv_dtype dtype, void* stream);
+
+/*
  * Debug/test helper: materialise one KV head's keys of a set of sequences
  * contiguously, through the block tables:
  *   dst[s][t][:] = cache[block_tables[s][t / B]][kv_head][t % B][:],  t < context_lens[s],
@@ -309,6 +327,18 @@ int pkv_bm_append_batch(pkv_block_manager* bm, const int32_t* seqs, int32_t n, i
                         int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs, int32_t* num_done);
 /* Release a finished sequence's blocks. */
 int pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq);
+/* Swapping ("pagedattention vllm" glossary, Memory Management > Swapping:
+ * blocks move to CPU memory to serve more sequences than the GPU holds):
+ * move sequence `seq` from manager `from` to manager `to` (say, the GPU
+ * pool's and a pinned host pool's).  Each of its blocks gets a fresh block
+ * of `to` (front of its free list, table order) and loses this sequence's
+ * reference in `from`; released entries (-1) stay -1; the id and length
+ * move along.  pairs[2k], pairs[2k+1] receive (block in from, block in to)
+ * for pkv_swap_blocks, *num_pairs their number.  PKV_ERR_NO_BLOCKS (too few
+ * free blocks in `to`) and every other error leave both managers as they
+ * were.  Shared blocks are copied for this sequence, not shared in `to`. */
+int pkv_bm_move_seq(pkv_block_manager* from, pkv_block_manager* to, int32_t seq, int32_t* pairs,
+                    int32_t pairs_cap, int32_t* num_pairs);
 /* Sliding window ("pagedattention vllm" glossary, Advanced Features >
  * Sliding Window: keep only recent blocks): release the blocks of `seq` that
  * hold no token of its last `window` tokens, i.e. table positions

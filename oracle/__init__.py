@@ -31,11 +31,11 @@ No function is "parity unpinned".
 """
 from .formats import E4M3_MAX, decode, decode_e4m3, quantize_e4m3
 from .attention import gather_sequence, paged_attention_decode
-from .cache_ops import copy_blocks, reshape_and_cache, reshape_and_cache_fp8
+from .cache_ops import copy_blocks, reshape_and_cache, reshape_and_cache_fp8, swap_blocks
 from .block_manager import BlockManager, NoFreeBlocks, BlockManagerError
 
 __all__ = [
-    "E4M3_MAX", "decode", "decode_e4m3", "quantize_e4m3", "reshape_and_cache_fp8",
+    "E4M3_MAX", "decode", "decode_e4m3", "quantize_e4m3", "reshape_and_cache_fp8", "swap_blocks",
     "decode", "gather_sequence", "paged_attention_decode", "copy_blocks", "reshape_and_cache",
     "BlockManager", "NoFreeBlocks", "BlockManagerError",
 ]

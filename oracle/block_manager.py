@@ -102,6 +102,34 @@ class BlockManager:
                 self.free.appendleft(b)
         del self.lengths[seq]
 
+    def move_seq(self, other: "BlockManager", seq: int):
+        """Move a sequence to another pool ("Memory Management > Swapping":
+        blocks swap between GPU and CPU memory).  Each of its blocks gets a
+        fresh block of `other` (taken from its free list in table order) and
+        loses this sequence's reference here; released entries (-1) stay -1.
+        Returns the (block here, block there) pairs to copy.  The sequence id
+        moves with it.  If `other` lacks free blocks nothing changes."""
+        if seq not in self.tables or seq in other.tables:
+            raise BlockManagerError("move needs a sequence here and its id free there")
+        if other.block_size != self.block_size:
+            raise BlockManagerError("pools of different block sizes")
+        table = self.tables[seq]
+        live = [b for b in table if b >= 0]
+        if len(other.free) < len(live):
+            raise NoFreeBlocks("destination pool exhausted")
+        pairs, new_table = [], []
+        for b in table:
+            if b < 0:
+                new_table.append(-1)
+                continue
+            nb = other._take()
+            pairs.append((b, nb))
+            new_table.append(nb)
+        other.tables[seq] = new_table
+        other.lengths[seq] = self.lengths[seq]
+        self.free_seq(seq)
+        return pairs
+
     def slide_window(self, seq: int, window: int) -> int:
         """Release the blocks that hold no token of the last `window` tokens
         ("pagedattention vllm" glossary, "Advanced Features > Sliding Window":

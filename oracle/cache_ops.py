@@ -74,3 +74,22 @@ def reshape_and_cache_fp8(k, v, k_cache, v_cache, slot_mapping, block_size: int,
             raise ValueError(f"slot {slot} outside the pool")
         k_cache[block, :, offset, :] = kq[i]
         v_cache[block, :, offset, :] = vq[i]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs) -> None:
+    """In place: block dst of the destination pools becomes a bitwise copy of
+    block src of the source pools, for each (src, dst) pair ("pagedattention
+    vllm" glossary, "Memory Management > Swapping": blocks move between GPU
+    memory and CPU memory to serve more sequences than the GPU holds).  The
+    two pools are different arrays, so any pair order gives one result as
+    long as destinations are distinct."""
+    pairs = [tuple(map(int, p)) for p in np.asarray(pairs).reshape(-1, 2)]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("swap pairs need distinct destinations")
+    sk, sv, dk, dv = _bits(src_k), _bits(src_v), _bits(dst_k), _bits(dst_v)
+    for src, dst in pairs:
+        if not (0 <= src < sk.shape[0] and 0 <= dst < dk.shape[0]):
+            raise ValueError("block id outside a pool")
+        dk[dst] = sk[src]
+        dv[dst] = sv[src]

@@ -22,10 +22,11 @@ from .ops import (
     paged_attention_decode,
     reshape_and_cache,
     reshape_and_cache_fp8,
+    swap_blocks,
     workspace_bytes,
 )
 
 __all__ = [
     "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
-    "paged_attention_decode", "reshape_and_cache", "reshape_and_cache_fp8", "workspace_bytes",
+    "paged_attention_decode", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
 ]

@@ -57,6 +57,9 @@ def load(path: str = LIB_PATH):
                                                      c_i32, ctypes.c_int, c_f32, c_f32, c_vp]),
         "pkv_copy_blocks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                            c_vp]),
+        "pkv_swap_blocks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                           ctypes.c_int, c_vp]),
+        "pkv_bm_move_seq": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i32p, c_i32, c_i32p]),
         "pkv_gather_kv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          c_i32, c_i32, ctypes.c_int, c_vp]),
         "pkv_bm_create": (c_vp, [c_i32, c_i32, c_i32, c_i32p]),

@@ -152,6 +152,20 @@ int launch_status(hipError_t e) {
 // check after a launch reports that launch only.
 void clear_pending_error() { (void)hipGetLastError(); }
 
+// A kernel may address `p` as is: device memory, or pinned host memory that
+// the runtime maps at the same address on the device.  Pageable host memory
+// and unknown pointers are refused instead of being dereferenced.
+bool device_addressable(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice) return true;
+  return a.type == hipMemoryTypeHost && a.devicePointer != nullptr &&
+         a.devicePointer == a.hostPointer;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +385,31 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, 
   clear_pending_error();
   return launch_status(pkv::launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs,
                                                block_bytes, num_blocks,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int pkv_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                    const int32_t* src_dst_pairs, int32_t num_pairs, int32_t num_src_blocks,
+                    int32_t num_dst_blocks, int32_t num_kv_heads, int32_t block_size,
+                    int32_t head_dim, pkv_dtype dtype, void* stream) {
+  const int es = dtype_bytes(dtype);
+  if (!es) return PKV_ERR_DTYPE;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_src_blocks < 0 ||
+      num_dst_blocks < 0)
+    return PKV_ERR_SHAPE;
+  if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !src_dst_pairs) return PKV_ERR_NULL;
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return PKV_ERR_ALIGN;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * es;
+  if ((int64_t)num_pairs * 2 * ((block_bytes + 16383) / 16384) > kMaxGrid) return PKV_ERR_SHAPE;
+  if (!device_addressable(dst_k) || !device_addressable(dst_v) || !device_addressable(src_k) ||
+      !device_addressable(src_v) || !device_addressable(src_dst_pairs))
+    return PKV_ERR_UNSUPPORTED;
+  clear_pending_error();
+  return launch_status(pkv::launch_swap_blocks(dst_k, dst_v, src_k, src_v, src_dst_pairs, num_pairs,
+                                               block_bytes, num_src_blocks, num_dst_blocks,
                                                static_cast<hipStream_t>(stream)));
 }
 

@@ -184,6 +184,43 @@ int pkv_bm_free_seq(pkv_block_manager* bm, int32_t seq) {
   return PKV_OK;
 }
 
+int pkv_bm_move_seq(pkv_block_manager* from, pkv_block_manager* to, int32_t seq, int32_t* pairs,
+                    int32_t pairs_cap, int32_t* num_pairs) {
+  if (!from || !to || !num_pairs) return PKV_ERR_NULL;
+  *num_pairs = 0;
+  if (from == to || !live(from, seq) || !seq_ok(to, seq) || to->length[seq] >= 0 ||
+      to->block_size != from->block_size)
+    return PKV_ERR_STATE;
+  const std::vector<int32_t>& table = from->tables[seq];
+  int32_t n = 0;
+  for (int32_t b : table) n += b >= 0;
+  if (n > pairs_cap) return PKV_ERR_CAPACITY;
+  if (n > 0 && !pairs) return PKV_ERR_NULL;
+  if ((int64_t)to->free_list.size() < n) return PKV_ERR_NO_BLOCKS;
+  for (int32_t b : table)
+    if (b >= 0 && from->refcount[b] <= 0) return PKV_ERR_STATE;
+  std::vector<int32_t> moved;
+  try {
+    moved.reserve(table.size());
+  } catch (...) {
+    return PKV_ERR_STATE;
+  }
+  for (int32_t b : table) {
+    if (b < 0) {
+      moved.push_back(-1);
+      continue;
+    }
+    const int32_t nb = take(to);
+    pairs[2 * *num_pairs] = b;
+    pairs[2 * *num_pairs + 1] = nb;
+    ++*num_pairs;
+    moved.push_back(nb);
+  }
+  to->tables[seq].swap(moved);
+  to->length[seq] = from->length[seq];
+  return pkv_bm_free_seq(from, seq);
+}
+
 int pkv_bm_slide_window(pkv_block_manager* bm, int32_t seq, int32_t window) {
   if (!bm) return PKV_ERR_NULL;
   if (!live(bm, seq) || window <= 0) return PKV_ERR_STATE;

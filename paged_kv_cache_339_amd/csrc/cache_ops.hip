@@ -76,22 +76,22 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_ca
   return hipGetLastError();
 }
 
-// Each workgroup copies one 16 KiB piece of one block of one cache.
+// Each workgroup copies one 16 KiB piece of one block of one cache (keys or
+// values) from the source pools to the destination pools; copy_blocks uses
+// one pool as both, swap_blocks a device pool and a pinned host pool.
 constexpr int kCopyPiece = 16384;
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache,
-                                                          char* __restrict__ v_cache,
-                                                          const int32_t* __restrict__ pairs,
-                                                          int64_t block_bytes, int32_t pieces,
-                                                          int32_t num_blocks) {
+__global__ __launch_bounds__(256) void copy_pool_blocks_kernel(
+    char* __restrict__ dst_k, char* __restrict__ dst_v, const char* src_k, const char* src_v,
+    const int32_t* __restrict__ pairs, int64_t block_bytes, int32_t pieces, int32_t num_src,
+    int32_t num_dst) {
   const int pair = blockIdx.x / (2 * pieces);
   const int rest = blockIdx.x % (2 * pieces);
   const int which = rest / pieces, piece = rest % pieces;
   const int32_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
-  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
-  char* base = which ? v_cache : k_cache;
-  const char* from = base + (size_t)src * block_bytes;
-  char* to = base + (size_t)dst * block_bytes;
+  if ((unsigned)src >= (unsigned)num_src || (unsigned)dst >= (unsigned)num_dst) return;
+  const char* from = (which ? src_v : src_k) + (size_t)src * block_bytes;
+  char* to = (which ? dst_v : dst_k) + (size_t)dst * block_bytes;
   const int64_t begin = (int64_t)piece * kCopyPiece;
   u32x4 buf[kCopyPiece / (256 * 16)];
 #pragma unroll
@@ -106,14 +106,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_c
   }
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
-                              int64_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              int32_t num_src, int32_t num_dst, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
   const int32_t pieces = (int32_t)((block_bytes + kCopyPiece - 1) / kCopyPiece);
   const dim3 grid((unsigned)((int64_t)num_pairs * 2 * pieces));
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, static_cast<char*>(k_cache),
-                     static_cast<char*>(v_cache), pairs, block_bytes, pieces, num_blocks);
+  hipLaunchKernelGGL(copy_pool_blocks_kernel, grid, dim3(256), 0, stream, static_cast<char*>(dst_k),
+                     static_cast<char*>(dst_v), static_cast<const char*>(src_k),
+                     static_cast<const char*>(src_v), pairs, block_bytes, pieces, num_src, num_dst);
   return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+  return launch_swap_blocks(k_cache, v_cache, k_cache, v_cache, pairs, num_pairs, block_bytes,
+                            num_blocks, num_blocks, stream);
 }
 
 // One thread per 16-byte chunk of dst[s][t][:].

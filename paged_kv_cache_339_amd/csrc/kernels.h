@@ -84,6 +84,9 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     const int32_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t row_bytes, int32_t block_size,
                                     int32_t num_blocks, hipStream_t stream);
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              int32_t num_src, int32_t num_dst, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, int32_t num_blocks, hipStream_t stream);
 hipError_t launch_gather_kv(void* dst, const void* cache, const int32_t* block_tables,

@@ -208,6 +208,28 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     check(st, "copy_blocks")
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, src_dst_pairs, stream=None):
+    """Block dst of (dst_k, dst_v) becomes a copy of block src of (src_k,
+    src_v) for each pair.  Pools [N, Hkv, B, D] on the GPU or in pinned host
+    memory (pin_memory=True); pairs: int32 GPU tensor [P, 2]."""
+    torch = _torch()
+    Ns, Hkv, B, D = src_k.shape
+    Nd = dst_k.shape[0]
+    if tuple(dst_k.shape[1:]) != (Hkv, B, D) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools must share [Hkv, B, D]")
+    if not (src_k.dtype == src_v.dtype == dst_k.dtype == dst_v.dtype):
+        raise TypeError("pools must share a dtype")
+    for t, name in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v")):
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a contiguous GPU or pinned host tensor")
+    n = src_dst_pairs.shape[0]
+    st = lib.pkv_swap_blocks(ctypes.c_void_p(dst_k.data_ptr()), ctypes.c_void_p(dst_v.data_ptr()),
+                             ctypes.c_void_p(src_k.data_ptr()), ctypes.c_void_p(src_v.data_ptr()),
+                             _dev(src_dst_pairs, "src_dst_pairs", torch.int32) if n else None, n, Ns, Nd,
+                             Hkv, B, D, dtype_code(src_k), _stream(stream))
+    check(st, "swap_blocks")
+
+
 def gather_kv(cache, block_tables, context_lens, kv_head, max_context_len, out=None, stream=None):
     """Contiguous [S, max_context_len, D] copy of one KV head through the tables
     (rows past a sequence's length keep out's previous contents; zeros if out is None)."""
@@ -300,6 +322,15 @@ class BlockManager:
 
     def free_seq(self, seq):
         check(lib.pkv_bm_free_seq(self._h, seq), "bm_free_seq")
+
+    def move_seq(self, other: "BlockManager", seq):
+        """Move `seq` to `other` (swap out / in); returns the (block here,
+        block there) pairs to copy with swap_blocks, int32 [P, 2]."""
+        cap = max(1, -(-self.seq_len(seq) // self.block_size))
+        buf, ptr = _i32(np.zeros(2 * cap))
+        n = ctypes.c_int32()
+        check(lib.pkv_bm_move_seq(self._h, other._h, seq, ptr, cap, ctypes.byref(n)), "bm_move_seq")
+        return buf[: 2 * n.value].reshape(-1, 2).copy()
 
     def slide_window(self, seq, window):
         n = lib.pkv_bm_slide_window(self._h, seq, window)

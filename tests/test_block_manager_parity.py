@@ -140,3 +140,58 @@ def test_create_rejects_bad_free_order():
         pkv.BlockManager(4, 4, 2, [0, 1, 1, 2])
     with pytest.raises(ValueError):
         pkv.BlockManager(4, 0, 2)
+
+
+swap_ops = st.lists(st.tuples(st.sampled_from(["add", "append", "append", "fork", "free", "out", "in"]),
+                              st.integers(0, 5), st.integers(0, 5), st.integers(1, 20)), max_size=50)
+
+
+@settings(max_examples=120, deadline=None)
+@given(ops=swap_ops, Ng=st.integers(1, 24), Nc=st.integers(0, 24), B=st.sampled_from([2, 8]),
+       seed=st.integers(0, 2**16))
+def test_moves_between_two_pools_agree(ops, Ng, Nc, B, seed):
+    """Sequences swapped out to a second (host) pool and back: the C++ and
+    twin managers give the same pairs, tables, counts and free lists."""
+    rng = np.random.default_rng(seed)
+    og, oc = rng.permutation(Ng), rng.permutation(Nc)
+    cg, cc = pkv.BlockManager(Ng, B, 6, og), pkv.BlockManager(Nc, B, 6, oc)
+    tg, tc = oracle.BlockManager(Ng, B, og), oracle.BlockManager(Nc, B, oc)
+    for op, a, b, n in ops:
+        if op in ("out", "in"):
+            (cf, ct, tf, tt) = (cg, cc, tg, tc) if op == "out" else (cc, cg, tc, tg)
+            try:
+                want = tf.move_seq(tt, a)
+            except oracle.BlockManagerError:
+                with pytest.raises(pkv.PkvError):
+                    cf.move_seq(ct, a)
+                continue
+            got = cf.move_seq(ct, a)
+            assert got.tolist() == [list(p) for p in want]
+        elif op == "add":
+            if a in tg.tables or a in tc.tables:
+                continue
+            tg.add_seq(a)
+            cg.add_seq(a)
+        elif op == "fork":
+            if a not in tg.tables or b in tg.tables or b in tc.tables:
+                continue
+            tg.fork(a, b)
+            cg.fork(a, b)
+        elif op == "free":
+            if a not in tg.tables:
+                continue
+            tg.free_seq(a)
+            cg.free_seq(a)
+        else:
+            if a not in tg.tables:
+                continue
+            for _ in range(n):
+                try:
+                    want = tg.append(a)
+                except oracle.NoFreeBlocks:
+                    with pytest.raises(pkv.PkvError):
+                        cg.append(a)
+                    break
+                assert cg.append(a) == want
+        compare(cg, tg, list(tg.tables))
+        compare(cc, tc, list(tc.tables))

@@ -183,3 +183,41 @@ def test_shared_prefix_workload_is_what_the_block_manager_builds():
     assert pairs == [tuple(p) for p in lay.cow_pairs.tolist()]
     assert len(pairs) == (spp - 1) * (cfg.num_seqs // spp)
     check_invariants(bm)
+
+
+def test_swap_out_and_back_leaves_attention_bitwise_equal():
+    """A sequence moved to a host pool (blocks copied there) and back to the
+    device pool reads the same keys and values: attention is bit-identical,
+    and a move that finds too few free blocks changes nothing."""
+    import oracle
+    from synthetic import to_storage
+    rng = np.random.default_rng(12)
+    N, Nh, B, Hkv, D = 24, 16, 4, 2, 8
+    kc = to_storage(rng.standard_normal((N, Hkv, B, D)), "f16")
+    vc = to_storage(rng.standard_normal((N, Hkv, B, D)), "f16")
+    hk = np.zeros((Nh, Hkv, B, D), dtype=np.float16)
+    hv = np.zeros_like(hk)
+    dev, host = BlockManager(N, B, rng.permutation(N)), BlockManager(Nh, B, rng.permutation(Nh))
+    for s, L in enumerate([13, 6]):
+        dev.add_seq(s)
+        for _ in range(L):
+            dev.append(s)
+    dev.fork(0, 2)
+    q = to_storage(rng.standard_normal((1, 2, D)), "f16")
+
+    def attend(bm, k, v, s):
+        t = np.array([bm.block_table(s)], dtype=np.int32)
+        return oracle.paged_attention_decode(q, k, v, t, [bm.seq_len(s)], 0.3, B, Hkv, "f16")
+
+    before = attend(dev, kc, vc, 0)
+    oracle.swap_blocks(kc, vc, hk, hv, dev.move_seq(host, 0))
+    assert 0 not in dev.tables and np.array_equal(attend(host, hk, hv, 0), before)
+    assert dev.block_table(2) and all(dev.refcount[b] == 1 for b in dev.block_table(2)), "shared blocks keep fork 2"
+    pairs = host.move_seq(dev, 0)
+    oracle.swap_blocks(hk, hv, kc, vc, pairs)
+    assert np.array_equal(attend(dev, kc, vc, 0), before)
+    small = BlockManager(2, B)
+    snap = (dict(dev.tables), list(dev.refcount), list(dev.free))
+    with pytest.raises(NoFreeBlocks):
+        dev.move_seq(small, 0)
+    assert (dict(dev.tables), list(dev.refcount), list(dev.free)) == snap
