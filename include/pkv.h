@@ -124,10 +124,10 @@ typedef struct pkv_attn_options {
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes and
  * options: a 256-byte header and the work list (8 bytes per sequence and
- * partition), plus fp32 partition results (head_dim + 2 floats per
- * sequence, query head and partition) when a sequence can span several
- * partitions.  0 for an empty batch, and 0 on invalid arguments (the decode
- * call reports those). */
+ * partition), plus partition results when a sequence can span several
+ * partitions: per sequence, query head and partition, head_dim elements in
+ * the output format (dtype) and 2 floats.  0 for an empty batch, and 0 on
+ * invalid arguments (the decode call reports those). */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
                                            int32_t block_size, int32_t max_context_len,

@@ -131,7 +131,9 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   plan->ws_ml_off = plan->ws_o_off;
   if (plan->max_parts > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads * plan->max_parts;
-    plan->ws_ml_off = plan->ws_o_off + round_up(rows * head_dim * sizeof(float), 256);
+    // Partition outputs are kept in the output format: the split-K writes
+    // are the dearest bytes of a split (written into a saturated read stream).
+    plan->ws_ml_off = plan->ws_o_off + round_up(rows * head_dim * dtype_bytes(dtype), 256);
     plan->ws_bytes = plan->ws_ml_off + round_up(rows * 2 * sizeof(float), 256);
   } else {
     plan->ws_bytes = plan->ws_o_off;
@@ -235,7 +237,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   char* ws = static_cast<char*>(workspace);
   p.work = reinterpret_cast<pkv::WorkHeader*>(ws);
   p.pairs = reinterpret_cast<pkv::WorkPair*>(ws + plan.pairs_off);
-  p.ws_o = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_o_off) : nullptr;
+  p.ws_o = plan.max_parts > 1 ? static_cast<void*>(ws + plan.ws_o_off) : nullptr;
   p.ws_ml = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_ml_off) : nullptr;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634 * (plan.fp8 ? (double)opts->k_scale : 1.0));
   p.v_scale = plan.fp8 ? opts->v_scale : 1.f;

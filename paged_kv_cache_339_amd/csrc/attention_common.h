@@ -86,7 +86,12 @@ struct MergeSmem {
 // After every wave has put its (m, l, o) for the G heads into `sm`: merge the
 // waves and store.  A sequence with one partition gets its final output row;
 // otherwise the partition's normalised output and (m, l) go to the
-// workspace for the reduce kernel.
+// workspace for the reduce kernel, laid out [S, Hkv, P, G, D] (in the
+// output format) and [S, Hkv, P, G, 2] (fp32): one workgroup's G rows form
+// one contiguous run, and the partitions of a (sequence, KV head) follow each
+// other.  Written into the saturated read stream of the other workgroups,
+// these bytes cost far more than their share of the traffic, so they are
+// kept as narrow as the output itself.
 template <int DT, int D, int G, int NW>
 __device__ __forceinline__ void merge_and_store(const AttnParams& p, const MergeSmem<D, G, NW>& sm,
                                                 int s, int h, int part, int nparts) {
@@ -107,15 +112,14 @@ __device__ __forceinline__ void merge_and_store(const AttnParams& p, const Merge
       o = fmaf(sm.o[w][g][d], a, o);
     }
     const float r = bad ? __builtin_nanf("") : o / tot * p.v_scale;
-    const int hq = h * G + g;
     if (nparts == 1) {
-      store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + hq) * D + d, r);
+      store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + h * G + g) * D + d, r);
     } else {
-      const size_t slot = ((size_t)s * p.num_q_heads + hq) * p.max_parts + part;
-      p.ws_o[slot * D + d] = r;
+      const size_t row0 = (((size_t)s * p.num_kv_heads + h) * p.max_parts + part) * G;
+      store_elem<DT>(p.ws_o, row0 * D + idx, r);
       if (d == 0) {
-        p.ws_ml[slot * 2] = M;
-        p.ws_ml[slot * 2 + 1] = bad ? __builtin_nanf("") : tot;
+        p.ws_ml[(row0 + g) * 2] = M;
+        p.ws_ml[(row0 + g) * 2 + 1] = bad ? __builtin_nanf("") : tot;
       }
     }
   }

@@ -92,6 +92,28 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 
   const WorkItem it = work_item(p);
   if (!it.valid) return;
+  const int lane = lane_id(), w = wave_id();
+
+  // Table entries of a 64-block window of the partition, one per lane; a
+  // token's block is then a lane shuffle away.  The first window is fetched
+  // before the sequence length arrives (it lies inside the row whatever the
+  // length, and is exact unless a sliding window starts the partition later),
+  // so the two loads overlap.
+  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const int b0_guess = it.part * p.part_blocks;
+  int tab = b0_guess + lane < p.max_blocks_per_seq ? table[b0_guess + lane] : -1;
+
+  // Query rows of the G heads (the B operand of the score product), also
+  // fetched before the length.
+  const int r = lane & 15, q = lane >> 4;
+  u32x4 qb[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = (r < G) ? load16(qrow + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+  }
+
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
     if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
@@ -103,17 +125,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   }
   if (it.part >= sw.nparts) return;
 
-  const int lane = lane_id(), w = wave_id();
-  const int r = lane & 15, q = lane >> 4;
   const int Hkv = p.num_kv_heads, L = sw.L, t0 = sw.t0, N = p.num_blocks;
-
-  u32x4 qb[KS];
-  {
-    const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = (r < G) ? load16(qrow + 32 * ks * ES) : u32x4{0, 0, 0, 0};
-  }
 
   f32x4 o[DPL];
 #pragma unroll
@@ -121,7 +133,6 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   float m = -INFINITY, l = 0.f;
   int bad = 0;
 
-  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const char* kbase = reinterpret_cast<const char*>(p.k_cache);
   const char* vbase = reinterpret_cast<const char*>(p.v_cache);
   // Chunks start on a block boundary (the block of t0 for the first
@@ -133,11 +144,10 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   const int te = min(L, tb + p.part_blocks * B);
   const int nch = (te - tb + CH - 1) / CH;
 
-  // Table entries of a 64-block window of the partition, one per lane; a
-  // token's block is then a lane shuffle away.  The window moves forward
-  // when a chunk reaches past it (wave-uniform).
+  // The table window moves forward when a chunk reaches past it
+  // (wave-uniform).  Entries past pb1 are never used.
   int tab_base = pb0;
-  int tab = pb0 + lane < pb1 ? table[pb0 + lane] : -1;
+  if (pb0 != b0_guess) tab = pb0 + lane < pb1 ? table[pb0 + lane] : -1;
 
   // Wave w takes U consecutive chunks at a time; the key and value loads of
   // all U are issued before the first is used.
@@ -261,7 +271,12 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kMfmaWaves = 4;
+// Waves per workgroup.  1 and 2 measured no faster with 512-token
+// partitions and slower with long ones.
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4
+#endif
+constexpr int kMfmaWaves = PKV_MFMA_WAVES;
 // 32-token chunks a wave loads ahead.  2 (204 VGPRs, still 2 waves per
 // SIMD) measured within +-4% of 1 across the GQA and sliding-window layers.
 #ifndef PKV_MFMA_UNROLL

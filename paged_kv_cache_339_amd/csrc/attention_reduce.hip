@@ -5,37 +5,84 @@
 // which is the softmax over all of the sequence's tokens (the block-by-block
 // evaluation the "pagedattention vllm" glossary describes under Attention
 // Computation, Block-Wise Attention, carried across workgroups).
-// One workgroup per (sequence, query head), one lane per element of the head.
 #include "attention_common.h"
 
 namespace pkv {
 
+// One workgroup per (sequence, KV head): the G query heads' partials of a
+// partition are one contiguous run, read 4 elements per lane.  The merge runs over the partitions in order, as online softmax:
+// M' = max(M, m_p), W = W 2^(M - M') + l_p 2^(m_p - M'), and O likewise with
+// l_p 2^(m_p - M') o_p; the result O / W equals the two-pass form above.
+constexpr int kReduceThreads = 256;
+
+// Four consecutive partition-output elements (stored in the output format).
+template <int DT>
+__device__ __forceinline__ float4 load4(const void* base, size_t idx) {
+  if constexpr (DT == PKV_F32) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    return make_float4(widen_half<DT>(w.x, false), widen_half<DT>(w.x, true),
+                       widen_half<DT>(w.y, false), widen_half<DT>(w.y, true));
+  }
+}
+constexpr int kReduceAhead = 4;     // partitions whose loads are in flight together
+
 template <int DT, int D>
-__global__ __launch_bounds__(D) void attn_reduce_kernel(AttnParams p, int B) {
-  const int s = blockIdx.x / p.num_q_heads;
-  const int hq = blockIdx.x % p.num_q_heads;
+__global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams p, int B) {
+  const int Hkv = p.num_kv_heads;
+  const int G = p.num_q_heads / Hkv;
+  const int s = blockIdx.x / Hkv;
+  const int h = blockIdx.x - s * Hkv;
   const SeqWork sw = seq_work(p, s, B);
   if (sw.bad || sw.nparts <= 1) return;     // written by the main kernel
-  const size_t base = ((size_t)s * p.num_q_heads + hq) * p.max_parts;
-  const float* ml = p.ws_ml + base * 2;
-  float M = -INFINITY;
-  for (int i = 0; i < sw.nparts; ++i) M = fmaxf(M, ml[2 * i]);
-  const float ref = softmax_ref(M);
-  const int d = threadIdx.x;
-  float tot = 0.f, o = 0.f;
-  for (int i = 0; i < sw.nparts; ++i) {
-    const float wgt = ml[2 * i + 1] * fast_exp2(ml[2 * i] - ref);
-    tot += wgt;
-    o = fmaf(wgt, p.ws_o[(base + i) * D + d], o);
+  const size_t run0 = ((size_t)s * Hkv + h) * p.max_parts;   // partition 0's first row is run0 * G
+  for (int e = threadIdx.x * 4; e < G * D; e += blockDim.x * 4) {
+    const int g = e / D, d = e - g * D;
+    float M = -INFINITY, W = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < sw.nparts; i0 += kReduceAhead) {
+      float m[kReduceAhead], l[kReduceAhead];
+      float4 o[kReduceAhead];
+#pragma unroll
+      for (int k = 0; k < kReduceAhead; ++k) {
+        const int i = min(i0 + k, sw.nparts - 1);
+        const size_t row = (run0 + i) * G + g;
+        m[k] = p.ws_ml[row * 2];
+        l[k] = p.ws_ml[row * 2 + 1];
+        o[k] = load4<DT>(p.ws_o, row * D + d);
+      }
+#pragma unroll
+      for (int k = 0; k < kReduceAhead; ++k) {
+        if (i0 + k >= sw.nparts) break;
+        const float Mn = fmaxf(M, m[k]);
+        const float ref = softmax_ref(Mn);
+        const float a = fast_exp2(M - ref);
+        const float b = l[k] * fast_exp2(m[k] - ref);
+        W = fmaf(W, a, b);
+        O.x = fmaf(O.x, a, o[k].x * b);
+        O.y = fmaf(O.y, a, o[k].y * b);
+        O.z = fmaf(O.z, a, o[k].z * b);
+        O.w = fmaf(O.w, a, o[k].w * b);
+        M = Mn;
+      }
+    }
+    const size_t out0 = ((size_t)s * p.num_q_heads + h * G + g) * D + d;
+    store_elem<DT>(p.out, out0, O.x / W);
+    store_elem<DT>(p.out, out0 + 1, O.y / W);
+    store_elem<DT>(p.out, out0 + 2, O.z / W);
+    store_elem<DT>(p.out, out0 + 3, O.w / W);
   }
-  store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + hq) * D + d, o / tot);
 }
 
 namespace {
 template <int DT, int D>
 hipError_t launch_reduce(const AttnParams& p, int B, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_q_heads));
-  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(D), 0, st, p, B);
+  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads));
+  // Lanes take 4 elements each; small groups need fewer lanes.
+  const int rows = (p.num_q_heads / p.num_kv_heads) * D / 4;
+  const int threads = min(kReduceThreads, max(kWave, (rows + kWave - 1) / kWave * kWave));
+  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(threads), 0, st, p, B);
   return hipGetLastError();
 }
 

@@ -29,8 +29,8 @@ struct AttnParams {
   const void* v_cache;
   const int32_t* block_tables;  // [S, M]
   const int32_t* context_lens;  // [S]
-  float* ws_o;                // [S, Hq, P, D] partition outputs, normalised
-  float* ws_ml;               // [S, Hq, P, 2]  (running max in log2 units, sum)
+  void* ws_o;                 // [S, Hkv, P, G, D] partition outputs, normalised, output format
+  float* ws_ml;               // [S, Hkv, P, G, 2] (running max in log2 units, sum)
   WorkHeader* work;           // plan written by the plan kernel
   WorkPair* pairs;            // [max_pairs]
   float scale_log2;           // scale * log2(e), times k_scale for 8-bit caches

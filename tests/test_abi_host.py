@@ -82,15 +82,18 @@ def _up(x):
 
 
 def test_workspace_sizes():
-    """Header (256 B) + work list (8 B per sequence and partition) + fp32
-    partition outputs and (m, l) when a sequence can span several partitions."""
+    """Header (256 B) + work list (8 B per sequence and partition) + partition
+    outputs in the output format and fp32 (m, l) when a sequence can span
+    several partitions."""
     ws = pkv.workspace_bytes
     assert ws(4, 2, 2, 64, 16, 64, 0) == 256 + _up(4 * 8)              # one partition: list only
     assert ws(0, 2, 2, 64, 16, 64, 0) == 0                              # empty batch
     n = ws(64, 32, 32, 128, 16, 2048, 1, partition_size=256)
     parts = 2048 // 256
     rows = 64 * 32 * parts
-    assert n == 256 + _up(64 * parts * 8) + _up(rows * 128 * 4) + _up(rows * 2 * 4)
+    assert n == 256 + _up(64 * parts * 8) + _up(rows * 128 * 2) + _up(rows * 2 * 4)   # fp16 outputs
+    n32 = ws(64, 32, 32, 128, 16, 2048, 0, partition_size=256)
+    assert n32 == 256 + _up(64 * parts * 8) + _up(rows * 128 * 4) + _up(rows * 2 * 4)
     assert ws(64, 32, 32, 128, 16, 2048, 1, partition_size=512) < n
     assert ws(256, 64, 8, 128, 32, 32768, 2) > 0                        # MFMA, split-K
     assert ws(4, 2, 2, 96, 16, 64, 0) == 0                              # invalid -> 0
