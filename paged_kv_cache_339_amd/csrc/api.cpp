@@ -3,6 +3,7 @@
 // kernel launched on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -325,6 +326,12 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
   a.head_dim = head_dim;
   a.k_scale = fp8 ? opts->k_scale : 1.f;
   a.v_scale = fp8 ? opts->v_scale : 1.f;
+  // Workgroups of 64 lanes per new token: about two 16-byte pieces per lane,
+  // one for 8-bit caches (each code takes an IEEE division).
+  const int64_t per_tok = (int64_t)(num_kv_heads > 0 ? num_kv_heads : 1) * a.chunks;
+  const int64_t per_wg = 64 * (fp8 ? 1 : 2);
+  a.split = (int32_t)std::min<int64_t>(16, std::max<int64_t>(1, (per_tok + per_wg - 1) / per_wg));
+  if ((int64_t)num_seqs * a.split + 1 > kMaxGrid) return PKV_ERR_SHAPE;
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                      num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                      max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts, stream, &a);

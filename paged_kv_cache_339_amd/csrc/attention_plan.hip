@@ -149,31 +149,34 @@ __device__ __forceinline__ void plan_body(const AttnParams& p, int B) {
 
 __global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) { plan_body(p, B); }
 
-// A decode step's first launch: workgroup 0 builds the work list, workgroup
-// 1 + i stores sequence i's new token.  Neither reads what the other writes
-// (the plan reads only context_lens), so they share one launch.
+// A decode step's first launch: workgroup 0 builds the work list, the next
+// a.split workgroups store sequence 0's new token, the next a.split
+// sequence 1's, and so on.  Neither part reads what the other writes (the
+// plan reads only context_lens), so they share one launch.
 __global__ __launch_bounds__(kWave) void append_and_plan_kernel(AttnParams p, int B, AppendArgs a) {
   if (blockIdx.x == 0) {
     plan_body(p, B);
     return;
   }
-  const int i = blockIdx.x - 1;
+  const int i = (blockIdx.x - 1) / a.split;
+  const int first = (blockIdx.x - 1 - i * a.split) * kWave + threadIdx.x;
+  const int stride = a.split * kWave;
   if (!a.fp8) {
-    scatter_token(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads, a.chunks, B,
-                  a.num_slots);
+    scatter_token(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, first, stride, p.num_kv_heads,
+                  a.chunks, B, a.num_slots);
   } else if (a.in_dtype == PKV_F16) {
-    scatter_token_fp8<PKV_F16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads,
-                               a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
+    scatter_token_fp8<PKV_F16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, first, stride,
+                               p.num_kv_heads, a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
   } else if (a.in_dtype == PKV_BF16) {
-    scatter_token_fp8<PKV_BF16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, p.num_kv_heads,
-                                a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
+    scatter_token_fp8<PKV_BF16>(a.k, a.v, a.k_cache, a.v_cache, a.slot_mapping, i, first, stride,
+                                p.num_kv_heads, a.head_dim, B, a.num_slots, a.k_scale, a.v_scale);
   }
 }
 
 hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL(append_and_plan_kernel, dim3((unsigned)p.num_seqs + 1), dim3(kWave), 0, stream,
-                     p, block_size, a);
+  const unsigned grid = (unsigned)((int64_t)p.num_seqs * a.split + 1);
+  hipLaunchKernelGGL(append_and_plan_kernel, dim3(grid), dim3(kWave), 0, stream, p, block_size, a);
   return hipGetLastError();
 }
 

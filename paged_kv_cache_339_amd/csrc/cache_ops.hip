@@ -13,8 +13,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
     int32_t chunks, int32_t block_size, int64_t num_slots) {
-  scatter_token(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, num_kv_heads, chunks, block_size,
-                num_slots);
+  scatter_token(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, threadIdx.x, blockDim.x,
+                num_kv_heads, chunks, block_size, num_slots);
 }
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int64_t num_slots, float k_scale, float v_scale) {
-  scatter_token_fp8<IT>(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, num_kv_heads, head_dim,
-                        block_size, num_slots, k_scale, v_scale);
+  scatter_token_fp8<IT>(k, v, k_cache, v_cache, slot_mapping, blockIdx.x, threadIdx.x, blockDim.x,
+                        num_kv_heads, head_dim, block_size, num_slots, k_scale, v_scale);
 }
 
 hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,

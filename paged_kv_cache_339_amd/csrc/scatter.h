@@ -9,28 +9,43 @@
 namespace pkv {
 
 // k_cache[slot / B][h][slot % B][:] = k[i][h][:] (and v) for every KV head h,
-// moved in 16-byte pieces by the threads of the calling workgroup.  A slot
-// outside [0, num_slots) stores nothing.  The slot and the first key/value
-// loads are independent, so they are in flight together.
+// moved in 16-byte pieces: the caller's thread takes pieces first,
+// first + stride, ... (stride = the threads given to the token, which may
+// span several workgroups).  A slot outside [0, num_slots) stores nothing.  The slot and every key/value load
+// of a thread (up to kScatterAhead pieces of each) are in flight together,
+// so a token costs one memory round trip, not one per piece.
+constexpr int kScatterAhead = 8;
+
 __device__ __forceinline__ void scatter_token(const char* __restrict__ k, const char* __restrict__ v,
                                               char* __restrict__ k_cache, char* __restrict__ v_cache,
                                               const int32_t* __restrict__ slot_mapping, int i,
-                                              int32_t num_kv_heads, int32_t chunks,
-                                              int32_t block_size, int64_t num_slots) {
+                                              int first, int stride, int32_t num_kv_heads,
+                                              int32_t chunks, int32_t block_size, int64_t num_slots) {
   const int32_t slot = slot_mapping[i];
   const int per_tok = num_kv_heads * chunks;        // 16-byte pieces of one token
   const char* ks = k + (size_t)i * per_tok * 16;
   const char* vs = v + (size_t)i * per_tok * 16;
-  const bool ok = slot >= 0 && (int64_t)slot < num_slots;
-  const int blk = ok ? slot / block_size : 0, off = ok ? slot % block_size : 0;
-  for (int j = threadIdx.x; j < per_tok; j += blockDim.x) {
-    const u32x4 a = load16(ks + (size_t)j * 16);
-    const u32x4 b = load16(vs + (size_t)j * 16);
-    if (!ok) continue;
-    const int h = j / chunks, c = j - h * chunks;
-    const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
-    store16(k_cache + dst, a);
-    store16(v_cache + dst, b);
+  for (int j0 = first; j0 < per_tok; j0 += stride * kScatterAhead) {
+    u32x4 a[kScatterAhead], b[kScatterAhead];
+#pragma unroll
+    for (int u = 0; u < kScatterAhead; ++u) {
+      const int j = j0 + u * stride;
+      if (j < per_tok) {
+        a[u] = load16(ks + (size_t)j * 16);
+        b[u] = load16(vs + (size_t)j * 16);
+      }
+    }
+    if (slot < 0 || (int64_t)slot >= num_slots) continue;
+    const int blk = slot / block_size, off = slot % block_size;
+#pragma unroll
+    for (int u = 0; u < kScatterAhead; ++u) {
+      const int j = j0 + u * stride;
+      if (j >= per_tok) break;
+      const int h = j / chunks, c = j - h * chunks;
+      const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
+      store16(k_cache + dst, a[u]);
+      store16(v_cache + dst, b[u]);
+    }
   }
 }
 
@@ -57,35 +72,53 @@ template <int IT>
 __device__ __forceinline__ void scatter_token_fp8(const char* __restrict__ k, const char* __restrict__ v,
                                                   char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                   const int32_t* __restrict__ slot_mapping, int i,
-                                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                  int first, int stride, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t block_size,
                                                   int64_t num_slots, float k_scale, float v_scale) {
   constexpr int ES = Format<IT>::kBytes;
   constexpr int LOADS = 16 * ES / 16;                 // 16-byte input loads per 16 codes
+  constexpr int AHEAD = kScatterAhead / 2;            // 16-code pieces whose inputs load together
   const int32_t slot = slot_mapping[i];
   const int chunks = head_dim / 16;                   // 16-code pieces per (token, head) row
   const int per_tok = num_kv_heads * chunks;
-  const bool ok = slot >= 0 && (int64_t)slot < num_slots;
-  const int blk = ok ? slot / block_size : 0, off = ok ? slot % block_size : 0;
-  for (int j = threadIdx.x; j < per_tok; j += blockDim.x) {
-    const char* ks = k + ((size_t)i * per_tok + j) * 16 * ES;
-    const char* vs = v + ((size_t)i * per_tok + j) * 16 * ES;
-    float kx[16], vx[16];
+  for (int j0 = first; j0 < per_tok; j0 += stride * AHEAD) {
+    u32x4 kr[AHEAD][LOADS], vr[AHEAD][LOADS];
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      widen16<IT>(load16(ks + 16 * l), kx + l * (16 / ES));
-      widen16<IT>(load16(vs + 16 * l), vx + l * (16 / ES));
-    }
-    if (!ok) continue;
-    u32x4 kc, vc;
+    for (int u = 0; u < AHEAD; ++u) {
+      const int j = j0 + u * stride;
+      if (j < per_tok) {
+        const char* ks = k + ((size_t)i * per_tok + j) * 16 * ES;
+        const char* vs = v + ((size_t)i * per_tok + j) * 16 * ES;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      kc[w] = e4m3_pack4<IT>(kx + 4 * w, k_scale);
-      vc[w] = e4m3_pack4<IT>(vx + 4 * w, v_scale);
+        for (int l = 0; l < LOADS; ++l) {
+          kr[u][l] = load16(ks + 16 * l);
+          vr[u][l] = load16(vs + 16 * l);
+        }
+      }
     }
-    const int h = j / chunks, c = j - h * chunks;
-    const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
-    store16(k_cache + dst, kc);
-    store16(v_cache + dst, vc);
+    if (slot < 0 || (int64_t)slot >= num_slots) continue;
+    const int blk = slot / block_size, off = slot % block_size;
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) {
+      const int j = j0 + u * stride;
+      if (j >= per_tok) break;
+      float kx[16], vx[16];
+#pragma unroll
+      for (int l = 0; l < LOADS; ++l) {
+        widen16<IT>(kr[u][l], kx + l * (16 / ES));
+        widen16<IT>(vr[u][l], vx + l * (16 / ES));
+      }
+      u32x4 kc, vc;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kc[w] = e4m3_pack4<IT>(kx + 4 * w, k_scale);
+        vc[w] = e4m3_pack4<IT>(vx + 4 * w, v_scale);
+      }
+      const int h = j / chunks, c = j - h * chunks;
+      const size_t dst = ((((size_t)blk * num_kv_heads + h) * block_size + off) * chunks + c) * 16;
+      store16(k_cache + dst, kc);
+      store16(v_cache + dst, vc);
+    }
   }
 }
 
