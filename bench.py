@@ -16,12 +16,15 @@ Prints ONE JSON line:
   value        KV GB/s read per step (sum(L) * Hkv * D * 2 * bytes / step time),
                from K steps timed between two HIP events
   roofline     the main attention kernel: algorithmic bytes per launch / its
-               average duration (HIP events around it on its stream, in a
-               second pass of K steps) vs 8 TB/s HBM
+               average duration vs 8 TB/s HBM.  The duration comes from a
+               second pass on the kernel's stream: K launches of the main
+               kernel alone, back to back between two HIP events (the work
+               list of the first pass reused), or, when a split-K reduce
+               follows it, events right before and after it in K steps
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
                on this host's cores (a reported baseline, not the target)
 
-    python bench.py [--steps K] [--warmup W] [--config {1..5}] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config N] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -209,6 +212,26 @@ def measured_traffic(kernel: str, workload: str):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def profiled_duration_us(kernel: str, workload: str):
+    """Average duration of `kernel` in the committed rocprofv3 kernel
+    statistics of `workload`, or None when there are none for the current
+    library sources."""
+    path = os.path.join(PROFILES, f"{kernel}__{workload}__kernel_stats.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    digest = [l.split(":", 1)[1].strip() for l in text if l.startswith("library_source_sha256:")]
+    if not digest or digest[0] != library_source_digest():
+        return None
+    for line in text:
+        if line.startswith(f"pkv::{kernel}"):
+            try:
+                return float(line.split()[-3])
+            except (IndexError, ValueError):
+                return None
+    return None
 
 
 def calibrate_copy(launches: int):
@@ -553,16 +576,19 @@ def main():
                 B, Hkv, S, Hq, D, layout.block_tables.shape[1], max_ctx, layout.num_blocks, code,
                 vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream))
 
+    def decode_args(opts):
+        """pkv_paged_attention_decode over the caches as the steps left them."""
+        return (vp(out.data_ptr()), vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()), vp(tables.data_ptr()),
+                vp(lens.data_ptr()), cfg.scale, B, Hkv, S, Hq, D, layout.block_tables.shape[1], max_ctx,
+                layout.num_blocks, code, vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream))
+
     K, W = args.steps, args.warmup
-    begins = [ev.create() for _ in range(K)]
-    ends = [ev.create() for _ in range(K)]
     win = cfg.sliding_window
     kvf = KV_FORMATS[cfg.kv_format]
-    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale)
-    timed = [AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win, kvf, cfg.k_scale, cfg.v_scale)
-             for i in range(K)]
+    chosen_part, parts_per_seq, kernel_used = pkv.plan_info(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, win,
+                                                            cfg.kv_format, cfg.k_scale, cfg.v_scale)
+    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 0)
     warm_args = step_args(plain)
-    timed_args = [step_args(o) for o in timed]
 
     def step(a):
         if copy_args is not None:
@@ -587,12 +613,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev.ms(t_start, t_stop)
-    # Pass 2: the same K steps again, with events right before and after the
-    # main attention kernel on its stream, for that kernel's duration.
-    for i in range(K):
-        step(timed_args[i])
-    torch.cuda.synchronize()
-    main_ms = [ev.ms(begins[i], ends[i]) for i in range(K)]
+    # Pass 2: the main attention kernel's duration.  Without a split-K reduce
+    # it runs K times back to back on the work list pass 1 left in the
+    # workspace (reuse_plan), between two events; with one, events go right
+    # before and after the main kernel inside each of K more steps.
+    if parts_per_seq == 1:
+        reuse = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 1)
+        dec = decode_args(reuse)
+        m0, m1 = ev.create(), ev.create()
+        ev.record(m0, stream)
+        for i in range(K):
+            st = lib.pkv_paged_attention_decode(*dec)
+            assert st == 0, st
+        ev.record(m1, stream)
+        torch.cuda.synchronize()
+        main_ms = [ev.ms(m0, m1) / K]
+        main_timing = "K back-to-back launches of the main kernel between two events"
+    else:
+        begins = [ev.create() for _ in range(K)]
+        ends = [ev.create() for _ in range(K)]
+        for i in range(K):
+            step(step_args(AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win, kvf, cfg.k_scale,
+                                       cfg.v_scale, 0)))
+        torch.cuda.synchronize()
+        main_ms = [ev.ms(begins[i], ends[i]) for i in range(K)]
+        main_timing = "events right before and after the main kernel in each of K steps"
     ev.close()
     assert torch.isfinite(out.float()).all().item(), "non-finite attention output"
 
@@ -604,8 +649,6 @@ def main():
     alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4   # es: q / out format
     achieved = alg_bytes / main_s / 1e9
     kv_gbps = step_kv / step_s / 1e9
-    kernel_used = args.kernel if args.kernel != "auto" else (
-        "mfma" if (cfg.dtype != "f32" and Hq // Hkv in (4, 8, 16)) else "valu")
     result = {
         "metric": METRIC,
         "value": round(kv_gbps, 2),
@@ -624,7 +667,8 @@ def main():
             "batch": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B,
             "kv_dtype": cfg.kv_dtype, "context_lens": LENGTH_DESC[args.config],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
-            "kv_bytes_per_step": step_kv, "partition_size": part, "kernel": kernel_used,
+            "kv_bytes_per_step": step_kv, "partition_size": part, "partition_tokens": chosen_part,
+            "partitions_per_seq": parts_per_seq, "kernel": kernel_used,
             "sliding_window": win, "kv_format": cfg.kv_format,
             "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
         },
@@ -641,6 +685,8 @@ def main():
             "traffic": measured_traffic(f"attn_{kernel_used}_kernel", cfg.name),
             "kernel": f"attn_{kernel_used}_kernel",
             "bytes_per_launch": int(alg_bytes),
+            "timing": main_timing,
+            "rocprof_avg_us": profiled_duration_us(f"attn_{kernel_used}_kernel", cfg.name),
         },
         "cpu_baseline": cpu,
     }

@@ -120,7 +120,28 @@ typedef struct pkv_attn_options {
   int32_t kv_format;
   float k_scale;
   float v_scale;
+  /* Nonzero: skip building the work list and use the one the workspace
+   * already holds, from an earlier call on the same stream with the same
+   * arguments except the data (out, q, caches, new tokens, slot mapping)
+   * and the same context_lens contents.  The list depends only on the batch
+   * (context_lens, max_context_len, block size, heads, partition, window,
+   * kernel), so the layers of one decode step can share it: build it on the
+   * first layer, reuse it on the others.  A stale list (changed lengths, or
+   * a workspace that never held one) leaves output rows undefined but stays
+   * memory-safe: every read is still bounded by the current context_lens,
+   * block tables and pool size. */
+  int32_t reuse_plan;
 } pkv_attn_options;
+
+/* What pkv_paged_attention_decode will launch for these sizes and options:
+ * the partition size in tokens after the automatic choice, the partitions
+ * per sequence its grid covers (1: no split-K reduce), and the main kernel
+ * (enum pkv_kernel, never PKV_KERNEL_AUTO).  Out-pointers may be NULL.
+ * Returns the status the decode call's argument checks would give. */
+int pkv_paged_attention_plan_info(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                  pkv_dtype dtype, const pkv_attn_options* opts,
+                                  int32_t* partition_size, int32_t* max_parts, int32_t* kernel);
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes and
  * options: a 256-byte header and the work list (8 bytes per sequence and

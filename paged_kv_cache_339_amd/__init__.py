@@ -20,6 +20,7 @@ from .ops import (
     decode_step,
     gather_kv,
     paged_attention_decode,
+    plan_info,
     reshape_and_cache,
     reshape_and_cache_fp8,
     swap_blocks,
@@ -28,5 +29,5 @@ from .ops import (
 
 __all__ = [
     "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
-    "paged_attention_decode", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
+    "paged_attention_decode", "plan_info", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
 ]

@@ -17,7 +17,7 @@ c_i32p = ctypes.POINTER(ctypes.c_int32)
 class AttnOptions(ctypes.Structure):
     _fields_ = [("partition_size", c_i32), ("kernel", c_i32),
                 ("main_begin_event", c_vp), ("main_end_event", c_vp), ("sliding_window", c_i32),
-                ("kv_format", c_i32), ("k_scale", c_f32), ("v_scale", c_f32)]
+                ("kv_format", c_i32), ("k_scale", c_f32), ("v_scale", c_f32), ("reuse_plan", c_i32)]
 
 
 class PkvError(RuntimeError):
@@ -46,6 +46,8 @@ def load(path: str = LIB_PATH):
         "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pkv_last_error": (ctypes.c_char_p, []),
         "pkv_paged_attention_workspace_bytes": (c_size, [c_i32] * 6 + [ctypes.c_int, ctypes.POINTER(AttnOptions)]),
+        "pkv_paged_attention_plan_info": (ctypes.c_int, [c_i32] * 6 + [ctypes.c_int, ctypes.POINTER(AttnOptions),
+                                                                      c_i32p, c_i32p, c_i32p]),
         "pkv_paged_attention_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32,
                                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                                       c_vp, c_size, ctypes.POINTER(AttnOptions), c_vp]),

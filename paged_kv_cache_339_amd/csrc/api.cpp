@@ -192,6 +192,20 @@ const char* pkv_status_str(int status) {
   }
 }
 
+int pkv_paged_attention_plan_info(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                  pkv_dtype dtype, const pkv_attn_options* opts,
+                                  int32_t* partition_size, int32_t* max_parts, int32_t* kernel) {
+  Plan plan;
+  const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, dtype, opts, &plan);
+  if (st != PKV_OK) return st;
+  if (partition_size) *partition_size = plan.part_blocks * block_size;
+  if (max_parts) *max_parts = plan.max_parts;
+  if (kernel) *kernel = plan.kernel;
+  return PKV_OK;
+}
+
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
                                            int32_t block_size, int32_t max_context_len,
@@ -256,8 +270,14 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int group = num_q_heads / num_kv_heads;
   clear_pending_error();
-  hipError_t err = append ? pkv::launch_append_and_plan(p, block_size, *append, s)
-                          : pkv::launch_attention_plan(p, block_size, s);
+  const bool reuse = opts && opts->reuse_plan;
+  hipError_t err = hipSuccess;
+  if (append) {
+    append->plan = reuse ? 0 : 1;
+    err = pkv::launch_append_and_plan(p, block_size, *append, s);
+  } else if (!reuse) {
+    err = pkv::launch_attention_plan(p, block_size, s);
+  }
   if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_begin_event) {
     const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
@@ -314,6 +334,7 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
   }
   const bool fp8 = opts && opts->kv_format == PKV_KV_FP8_E4M3;
   pkv::AppendArgs a;
+  a.plan = 1;
   a.k = static_cast<const char*>(k_new);
   a.v = static_cast<const char*>(v_new);
   a.k_cache = static_cast<char*>(k_cache);

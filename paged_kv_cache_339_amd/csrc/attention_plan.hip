@@ -149,13 +149,14 @@ __device__ __forceinline__ void plan_body(const AttnParams& p, int B) {
 
 __global__ __launch_bounds__(kWave) void attn_plan_kernel(AttnParams p, int B) { plan_body(p, B); }
 
-// A decode step's first launch: workgroup 0 builds the work list, the next
-// a.split workgroups store sequence 0's new token, the next a.split
-// sequence 1's, and so on.  Neither part reads what the other writes (the
-// plan reads only context_lens), so they share one launch.
+// A decode step's first launch: workgroup 0 builds the work list (unless the
+// caller reuses the one the workspace holds), the next a.split workgroups
+// store sequence 0's new token, the next a.split sequence 1's, and so on.
+// Neither part reads what the other writes (the plan reads only
+// context_lens), so they share one launch.
 __global__ __launch_bounds__(kWave) void append_and_plan_kernel(AttnParams p, int B, AppendArgs a) {
   if (blockIdx.x == 0) {
-    plan_body(p, B);
+    if (a.plan) plan_body(p, B);
     return;
   }
   const int i = (blockIdx.x - 1) / a.split;

@@ -70,6 +70,7 @@ struct AppendArgs {
   int32_t head_dim;
   float k_scale, v_scale;
   int32_t split;              // workgroups (of one wave) per new token, >= 1
+  int32_t plan;               // 0: workgroup 0 leaves the work list as it is
 };
 hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const AppendArgs& a,
                                   hipStream_t stream);

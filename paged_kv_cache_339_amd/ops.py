@@ -49,12 +49,26 @@ def _dev(t, name, dtype=None, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _options(partition_size, kernel, main_events, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
+def _options(partition_size, kernel, main_events, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,
+             reuse_plan=False):
     ev0, ev1 = (None, None) if main_events is None else main_events
     return AttnOptions(int(partition_size), KERNELS[kernel],
                        None if ev0 is None else ctypes.c_void_p(int(ev0)),
                        None if ev1 is None else ctypes.c_void_p(int(ev1)), int(sliding_window),
-                       KV_FORMATS[kv_format], float(k_scale), float(v_scale))
+                       KV_FORMATS[kv_format], float(k_scale), float(v_scale), int(bool(reuse_plan)))
+
+
+def plan_info(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, dtype_code_,
+              partition_size=0, kernel="auto", sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
+    """(partition_size, max_parts, kernel name) a decode call with these arguments launches."""
+    opts = _options(partition_size, kernel, None, sliding_window, kv_format, k_scale, v_scale)
+    part, parts, kern = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib.pkv_paged_attention_plan_info(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                           max_context_len, dtype_code_, ctypes.byref(opts), ctypes.byref(part),
+                                           ctypes.byref(parts), ctypes.byref(kern))
+    check(st, "plan_info")
+    names = {v: k for k, v in KERNELS.items()}
+    return part.value, parts.value, names[kern.value]
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
@@ -102,13 +116,16 @@ def _ws_args(workspace):
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, max_context_len, partition_size=0, kernel="auto",
                            workspace=None, stream=None, main_events=None, sliding_window=0, kv_format="same",
-                           k_scale=1.0, v_scale=1.0):
+                           k_scale=1.0, v_scale=1.0, reuse_plan=False):
     """out[s, j] = softmax(scale * q[s, j] K_s^T) V_s through the block tables.
 
     q, out: [S, Hq, D]; k_cache, v_cache: [N, Hkv, B, D]; block_tables int32
     [S, M]; context_lens int32 [S] (device); max_context_len: host int >=
     every context length.  `workspace`: optional uint8 device tensor of at
-    least workspace_bytes(...) bytes."""
+    least workspace_bytes(...) bytes.  reuse_plan: the workspace holds the
+    work list of an earlier call with the same batch (see pkv.h)."""
+    if reuse_plan and workspace is None:
+        raise ValueError("reuse_plan needs the workspace of the call that built the work list")
     torch = _torch()
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
@@ -117,7 +134,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
                            sliding_window, kv_format, k_scale, v_scale)
-    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan)
     st = lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
@@ -129,10 +146,13 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 
 def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
                 block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
-                stream=None, main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
+                stream=None, main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,
+                reuse_plan=False):
     """reshape_and_cache(k_new, v_new, ..., slot_mapping) followed by
     paged_attention_decode(...), with the token store and the attention work
     list in one launch.  k_new, v_new: [S, Hkv, D]; slot_mapping int32 [S]."""
+    if reuse_plan and workspace is None:
+        raise ValueError("reuse_plan needs the workspace of the call that built the work list")
     torch = _torch()
     S, Hq, D = q.shape
     N, Hkv, B, D2 = k_cache.shape
@@ -147,7 +167,7 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
                            sliding_window, kv_format, k_scale, v_scale)
-    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan)
     st = lib.pkv_decode_step(
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),

@@ -147,3 +147,28 @@ def test_automatic_partition_splits_only_small_batches():
     assert ws(256, 64, 8, 128, 32, 32768, 2) == one(256)                      # 2048 pairs, 32k tokens
     assert ws(64, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == one(64)  # window span 4112 tokens
     assert ws(4, 8, 8, 128, 16, 32768, 2) > one(4 * 32)                       # 32 pairs: split
+
+
+def test_plan_info_reports_the_launch():
+    """Partition size after the automatic choice, partitions per sequence and
+    kernel, for the stated workloads and a small batch that must split."""
+    info = pkv.plan_info
+    assert info(64, 32, 32, 128, 16, 2048, 1) == (2048, 1, "valu")              # llama2-7b layer
+    assert info(256, 64, 8, 128, 32, 32768, 2) == (32768, 1, "mfma")            # 70B-style GQA
+    assert info(256, 64, 8, 128, 32, 32768, 2, partition_size=512) == (512, 64, "mfma")
+    assert info(256, 64, 8, 128, 32, 32768, 2, kernel="valu") == (32768, 1, "valu")
+    assert info(64, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == (4112, 1, "mfma")
+    part, parts, kern = info(4, 8, 8, 128, 16, 32768, 2)
+    assert parts > 1 and part * parts >= 32768 and part % 16 == 0 and kern == "valu"
+    assert info(64, 32, 32, 128, 16, 2048, 1, partition_size=48) == (48, 43, "valu")
+    with pytest.raises(pkv.PkvError):
+        info(4, 2, 2, 96, 16, 64, 0)                                             # head_dim 96
+    with pytest.raises(pkv.PkvError):
+        info(4, 2, 2, 64, 16, 64, 0, kernel="mfma")                              # fp32 on MFMA
+    for args in [(64, 32, 32, 128, 16, 2048, 1), (4, 8, 8, 128, 16, 32768, 2)]:
+        part, parts, _ = info(*args)
+        want = 256 + _up(args[0] * parts * 8)
+        if parts > 1:
+            rows = args[0] * args[1] * parts
+            want += _up(rows * args[3] * (4 if args[6] == 0 else 2)) + _up(rows * 2 * 4)
+        assert pkv.workspace_bytes(*args) == want

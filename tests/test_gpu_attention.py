@@ -299,3 +299,61 @@ def test_decode_step_with_window():
     torch.cuda.synchronize()
     want, _, _ = oracle_step(lay, host)
     assert_rows_close(widen(out), want, cfg.dtype, "decode_step window")
+
+
+def _sign_flipped(t: torch.Tensor) -> torch.Tensor:
+    """The tensor with every element's sign bit flipped (an exact negation
+    for every format, E4M3 codes included)."""
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]
+    bits = {1: 0x80, 2: -0x8000, 4: -0x80000000}[t.element_size()]
+    return (t.view(view) ^ bits).view(t.dtype)
+
+
+@pytest.mark.parametrize("idx,partition_size", [(3, 0), (4, 0), (4, 256), (6, 0), (8, 0)])
+def test_reused_work_list_across_layers_is_bit_identical(idx, partition_size):
+    """The layers of one decode step share context lengths, tables and slots:
+    the work list built by the first layer's call serves the others
+    (reuse_plan), with outputs and stored tokens bit-identical to building
+    it on every call."""
+    cfg = CONFIGS[idx].scaled(**SCALED[idx])
+    lay = make_layout(cfg, seed=70 + idx)
+    base = DeviceStep.from_host(lay, host_values(lay))
+    part, parts, kern = pkv.plan_info(len(lay.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                      cfg.block_size, max(1, lay.max_context_len), pkv.ops.dtype_code(base.q),
+                                      partition_size, "auto", cfg.sliding_window, cfg.kv_format, cfg.k_scale,
+                                      cfg.v_scale)
+    say(f"reuse_plan config {idx} S={len(lay.context_lens)} partition={part} x{parts} kernel={kern}")
+
+    def layer(l):
+        f = [(lambda t: t), _sign_flipped]
+        fc, fq = f[l % 2], f[(l // 2) % 2]
+        return (fq(base.q).clone(), fc(base.k_cache).clone(), fc(base.v_cache).clone(),
+                fc(base.k_new).clone(), fc(base.v_new).clone())
+
+    kw = dict(partition_size=partition_size, sliding_window=cfg.sliding_window, kv_format=cfg.kv_format,
+              k_scale=cfg.k_scale, v_scale=cfg.v_scale)
+    common = (base.slots, base.tables, base.lens, cfg.scale, cfg.block_size, cfg.num_kv_heads,
+              max(1, lay.max_context_len))
+    ws = torch.empty(max(256, pkv.workspace_bytes(len(lay.context_lens), cfg.num_q_heads, cfg.num_kv_heads,
+                                                   cfg.head_dim, cfg.block_size, max(1, lay.max_context_len),
+                                                   pkv.ops.dtype_code(base.q), partition_size, "auto",
+                                                   cfg.sliding_window, cfg.kv_format, cfg.k_scale,
+                                                   cfg.v_scale)), dtype=torch.uint8, device="cuda")
+    view = {"f32": torch.int32, "fp8": torch.uint8}.get(cfg.kv_dtype, torch.int16)
+    oview = torch.int32 if cfg.dtype == "f32" else torch.int16
+    for l in range(4):
+        q, kc, vc, kn, vn = layer(l)
+        rq, rkc, rvc, rkn, rvn = layer(l)
+        out = torch.empty_like(q)
+        ref = torch.empty_like(q)
+        pkv.decode_step(out, q, kn, vn, kc, vc, *common, workspace=ws, reuse_plan=l > 0, **kw)
+        pkv.decode_step(ref, rq, rkn, rvn, rkc, rvc, *common, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(kc.view(view), rkc.view(view)) and torch.equal(vc.view(view), rvc.view(view)), l
+        assert torch.equal(out.view(oview), ref.view(oview)), l
+        again = torch.empty_like(q)
+        pkv.paged_attention_decode(again, q, kc, vc, base.tables, base.lens, cfg.scale, cfg.block_size,
+                                   cfg.num_kv_heads, max(1, lay.max_context_len), workspace=ws, reuse_plan=True,
+                                   **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(oview), ref.view(oview)), l
