@@ -519,6 +519,8 @@ def main():
     seed = args.config if args.seed is None else args.seed
     layout = make_layout(cfg, seed=seed)
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
+    # The workload's name, tagged when the partition differs from its stated one.
+    tag = cfg.name if part == cfg.partition_size else f"{cfg.name}_partition{part or 'auto'}"
     S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     es = DTYPE_BYTES[cfg.dtype]
     step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.kv_dtype, cfg.sliding_window)
@@ -663,7 +665,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name,
+            "workload": tag,
             "batch": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B,
             "kv_dtype": cfg.kv_dtype, "context_lens": LENGTH_DESC[args.config],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
@@ -682,11 +684,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(f"attn_{kernel_used}_kernel", cfg.name),
+            "traffic": measured_traffic(f"attn_{kernel_used}_kernel", tag),
             "kernel": f"attn_{kernel_used}_kernel",
             "bytes_per_launch": int(alg_bytes),
             "timing": main_timing,
-            "rocprof_avg_us": profiled_duration_us(f"attn_{kernel_used}_kernel", cfg.name),
+            "rocprof_avg_us": profiled_duration_us(f"attn_{kernel_used}_kernel", tag),
         },
         "cpu_baseline": cpu,
     }
