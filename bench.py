@@ -54,6 +54,7 @@ LENGTH_DESC = {
     5: "1000-token shared prompt + uniform [1, 512] per-sample tail",
     6: "uniform [1024, 16384], attention over the last 4096",
     8: "uniform [128, 2048]",
+    9: "uniform [1024, 32768]",
 }
 
 

@@ -83,9 +83,10 @@ const char* pkv_last_error(void);
 /* ------------------------------------------------------------------------ */
 
 enum pkv_kernel {
-  PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit data with 4..16 query heads per KV head, else VALU */
+  PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit queries with 4..16 query heads per KV head, else VALU */
   PKV_KERNEL_VALU = 1,  /* vector-ALU kernel: 1, 2, 4 or 8 query heads per KV head */
-  PKV_KERNEL_MFMA = 2   /* matrix-core kernel: f16/bf16, 4, 8 or 16 query heads per KV head */
+  PKV_KERNEL_MFMA = 2   /* matrix-core kernel: f16/bf16 queries (8-bit caches decoded to that
+                           format), 4, 8 or 16 query heads per KV head */
 };
 
 typedef struct pkv_attn_options {

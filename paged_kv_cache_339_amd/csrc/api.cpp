@@ -81,8 +81,8 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   const bool valu_group = group == 1 || group == 2 || group == 4 || group == 8;
   int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
   if (kernel == PKV_KERNEL_AUTO)
-    kernel = (sixteen_bit && mfma_group && !fp8) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
-  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group && !fp8)) return PKV_ERR_UNSUPPORTED;
+    kernel = (sixteen_bit && mfma_group) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
+  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group)) return PKV_ERR_UNSUPPORTED;
   if (fp8 && (block_size == 8 || block_size == 64)) return PKV_ERR_UNSUPPORTED;
   if (kernel == PKV_KERNEL_VALU && !valu_group) return PKV_ERR_UNSUPPORTED;
   if (kernel != PKV_KERNEL_MFMA && kernel != PKV_KERNEL_VALU) return PKV_ERR_SHAPE;
@@ -284,7 +284,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     if (e != hipSuccess) return launch_status(e);
   }
   const bool have = plan.kernel == PKV_KERNEL_MFMA
-                        ? pkv::launch_attention_mfma(p, dtype, head_dim, block_size, group, s, &err)
+                        ? pkv::launch_attention_mfma(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
+                                                     head_dim, block_size, group, s, &err)
                         : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
                                                      head_dim, block_size, group, s, &err);
   if (!have) return PKV_ERR_UNSUPPORTED;

@@ -28,6 +28,14 @@
 //    A operand row "element DPL r + n over those tokens"; the B operand is
 //    the lane's own eight softmax weights.  Output tile n then holds, in
 //    lane (r, q), head r at elements DPL(4q + i) + n.
+//
+// 8-bit (E4M3) caches: codes are decoded to the query's 16-bit format in
+// registers (v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1, exact for every
+// code; checked on all 256) and go through the same MFMA.  A lane's 16-byte
+// load of a key row then holds 16 codes, elements 64c + 16q .. +16: the
+// first eight feed k-step 2c, the last eight k-step 2c + 1, and the query
+// operand is read in that order.  The key scale is folded into the softmax
+// scale, the value scale into the output.
 #include "attention_common.h"
 
 namespace pkv {
@@ -55,6 +63,27 @@ template <> struct Mfma<PKV_F16> {
   static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_f16(x); }
 };
 
+// Four E4M3 codes (one dword) -> four 16-bit values of format DT (two dwords).
+template <int DT>
+__device__ __forceinline__ u32x2 decode4_e4m3(uint32_t w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == PKV_BF16) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
+  } else {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true))};
+  }
+}
+
+// Eight codes (two dwords) -> one 16-bit MFMA operand register group.
+template <int DT>
+__device__ __forceinline__ u32x4 decode8_e4m3(uint32_t w0, uint32_t w1) {
+  const u32x2 a = decode4_e4m3<DT>(w0), b = decode4_e4m3<DT>(w1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 template <int DPL> struct VRow;
 template <> struct VRow<8> {
   typedef u32x4 type;
@@ -70,6 +99,31 @@ template <> struct VRow<4> {
   static __device__ __forceinline__ type zero() { return u32x2{0, 0}; }
 };
 
+// A lane's DPL value elements of one token, as loaded (KT) and as the
+// 16-bit operand the transpose works on.
+template <int DT, int KT, int DPL> struct VLoad;
+template <int DT, int DPL> struct VLoad<DT, DT, DPL> {
+  typedef typename VRow<DPL>::type raw;
+  static __device__ __forceinline__ raw load(const char* p) { return VRow<DPL>::load(p); }
+  static __device__ __forceinline__ raw zero() { return VRow<DPL>::zero(); }
+  static __device__ __forceinline__ typename VRow<DPL>::type widen(raw x) { return x; }
+};
+template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 8> {
+  typedef u32x2 raw;
+  static __device__ __forceinline__ raw load(const char* p) { return VRow<4>::load(p); }
+  static __device__ __forceinline__ raw zero() { return u32x2{0, 0}; }
+  static __device__ __forceinline__ u32x4 widen(raw x) { return decode8_e4m3<DT>(x[0], x[1]); }
+};
+template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 4> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw load(const char* p) {
+    if constexpr (PKV_NT_KV) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    return *reinterpret_cast<const uint32_t*>(p);
+  }
+  static __device__ __forceinline__ raw zero() { return 0u; }
+  static __device__ __forceinline__ u32x2 widen(raw x) { return decode4_e4m3<DT>(x); }
+};
+
 // Waves per SIMD the register allocation must allow.  3 (168 registers,
 // no spills) helps only when partitions are short; with the default
 // partitions 2 measured up to 3% faster.
@@ -77,16 +131,19 @@ template <> struct VRow<4> {
 #define PKV_MFMA_OCC 2
 #endif
 
-template <int DT, int D, int B, int G, int NW, int U>
+template <int DT, int KT, int D, int B, int G, int NW, int U>
 __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(AttnParams p) {
-  constexpr int ES = 2;
+  constexpr int ES = 2;           // query / operand bytes per element
+  constexpr bool F8 = KT == PKV_FP8_E4M3;
+  constexpr int KES = F8 ? 1 : 2; // cache bytes per element
   constexpr int KS = D / 32;      // k-steps of the score product
+  constexpr int KL = F8 ? KS / 2 : KS;   // 16-byte key loads per token row and lane
   constexpr int DPL = D / 16;     // value elements per lane per token
   constexpr int CH = 32;          // tokens per chunk
   static_assert(G >= 1 && G <= 16, "query group must fit 16 MFMA columns");
   static_assert(B >= 8, "8 consecutive tokens of a lane must share a block");
   using Ops = Mfma<DT>;
-  using VR = VRow<DPL>;
+  using VL = VLoad<DT, KT, DPL>;
 
   __shared__ MergeSmem<D, G, NW> sm;
 
@@ -111,7 +168,12 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
     const char* qrow = reinterpret_cast<const char*>(p.q) +
                        (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = (r < G) ? load16(qrow + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) {
+      // Element offset of k-step ks past 8q: 32 ks, or for 8-bit caches
+      // 64 (ks / 2) + 8 q + 8 (ks % 2) (the order the key loads give).
+      const int off = F8 ? 64 * (ks / 2) + 8 * q + 8 * (ks % 2) : 32 * ks;
+      qb[ks] = (r < G) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
+    }
   }
 
   const SeqWork sw = seq_work(p, it.s, B);
@@ -159,10 +221,11 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
     }
 
     // Keys: lane (r, q) loads token 8(r/4) + 4t + r%4 of the chunk for t = 0, 1,
-    // head_dim elements 32s + 8q .. +8 for every k-step s.
-    u32x4 kr[U][2][KS];
+    // head_dim elements 32s + 8q .. +8 for every k-step s (8-bit caches:
+    // elements 64c + 16q .. +16 for k-steps 2c and 2c + 1).
+    u32x4 kr[U][2][KL];
     // Values: tokens 8q .. 8q+7 (one block), elements DPL r .. DPL r + DPL.
-    typename VR::type vr[U][8];
+    typename VL::raw vr[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // A chunk at or past te (the last group of a partition) loads nothing;
@@ -177,9 +240,11 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
           bad = 1;
           ok = false;
         }
-        const char* kp = kbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tok % B) * D + 8 * q) * ES;
+        const char* kp = kbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tok % B) * D +
+                                  (F8 ? 16 : 8) * q) * KES;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[u][t][ks] = ok ? load16_kv(kp + 32 * ks * ES) : u32x4{0, 0, 0, 0};
+        for (int kl = 0; kl < KL; ++kl)
+          kr[u][t][kl] = ok ? load16_kv(kp + (F8 ? 64 : 32) * kl * KES) : u32x4{0, 0, 0, 0};
       }
       const int tv0 = c0 + 8 * q;
       bool ok = tv0 < te && tv0 + 7 >= t0;
@@ -188,10 +253,10 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
         bad = 1;
         ok = false;
       }
-      const char* vp = vbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tv0 % B) * D + DPL * r) * ES;
+      const char* vp = vbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tv0 % B) * D + DPL * r) * KES;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        vr[u][j] = (ok && tv0 + j < te && tv0 + j >= t0) ? VR::load(vp + (size_t)j * D * ES) : VR::zero();
+        vr[u][j] = (ok && tv0 + j < te && tv0 + j >= t0) ? VL::load(vp + (size_t)j * D * KES) : VL::zero();
     }
 
 #pragma unroll
@@ -204,7 +269,16 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
       for (int t = 0; t < 2; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = Ops::mma(kr[u][t][ks], qb[ks], acc);
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 a;
+          if constexpr (F8) {
+            const u32x4 w = kr[u][t][ks / 2];
+            a = (ks % 2) ? decode8_e4m3<DT>(w[2], w[3]) : decode8_e4m3<DT>(w[0], w[1]);
+          } else {
+            a = kr[u][t][ks];
+          }
+          acc = Ops::mma(a, qb[ks], acc);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i] * p.scale_log2;
       }
@@ -236,13 +310,16 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
       }
       l = fmaf(l, alpha, ps);
 
+      typename VRow<DPL>::type v16[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v16[j] = VL::widen(vr[u][j]);
 #pragma unroll
       for (int n = 0; n < DPL; ++n) {
         u32x4 a;
         const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          a[k] = __builtin_amdgcn_perm(vr[u][2 * k + 1][n >> 1], vr[u][2 * k][n >> 1], sel);
+          a[k] = __builtin_amdgcn_perm(v16[2 * k + 1][n >> 1], v16[2 * k][n >> 1], sel);
         o[n] *= alpha;
         o[n] = Ops::mma(a, pb, o[n]);
       }
@@ -283,52 +360,72 @@ constexpr int kMfmaWaves = PKV_MFMA_WAVES;
 #define PKV_MFMA_UNROLL 1
 #endif
 
-template <int DT, int D, int B, int G>
+// Chunks loaded ahead per wave: 8-bit caches load half the bytes per chunk,
+// so two of their chunks keep the same bytes in flight as one 16-bit chunk.
+template <int KT>
+constexpr int mfma_unroll() {
+  return KT == PKV_FP8_E4M3 ? 2 * PKV_MFMA_UNROLL : PKV_MFMA_UNROLL;
+}
+
+template <int DT, int KT, int D, int B, int G>
 hipError_t launch_mfma(const AttnParams& p, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, D, B, G, kMfmaWaves, PKV_MFMA_UNROLL>), grid,
-                     dim3(kMfmaWaves * kWave), 0,
-                     st, p);
+  hipLaunchKernelGGL((attn_mfma_kernel<DT, KT, D, B, G, kMfmaWaves, mfma_unroll<KT>()>), grid,
+                     dim3(kMfmaWaves * kWave), 0, st, p);
   return hipGetLastError();
 }
 
-template <int DT, int D, int B>
+template <int DT, int KT, int D, int B>
 bool by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
   switch (G) {
-    case 4: *e = launch_mfma<DT, D, B, 4>(p, st); return true;
-    case 8: *e = launch_mfma<DT, D, B, 8>(p, st); return true;
-    case 16: *e = launch_mfma<DT, D, B, 16>(p, st); return true;
+    case 4: *e = launch_mfma<DT, KT, D, B, 4>(p, st); return true;
+    case 8: *e = launch_mfma<DT, KT, D, B, 8>(p, st); return true;
+    case 16: *e = launch_mfma<DT, KT, D, B, 16>(p, st); return true;
     default: return false;
   }
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 bool by_block(const AttnParams& p, int B, int G, hipStream_t st, hipError_t* e) {
-  switch (B) {
-    case 8: return by_group<DT, D, 8>(p, G, st, e);
-    case 16: return by_group<DT, D, 16>(p, G, st, e);
-    case 32: return by_group<DT, D, 32>(p, G, st, e);
-    case 64: return by_group<DT, D, 64>(p, G, st, e);
-    default: return false;
+  if constexpr (KT == PKV_FP8_E4M3) {
+    switch (B) {                      // 8-bit caches: 16- and 32-token blocks
+      case 16: return by_group<DT, KT, D, 16>(p, G, st, e);
+      case 32: return by_group<DT, KT, D, 32>(p, G, st, e);
+      default: return false;
+    }
+  } else {
+    switch (B) {
+      case 8: return by_group<DT, KT, D, 8>(p, G, st, e);
+      case 16: return by_group<DT, KT, D, 16>(p, G, st, e);
+      case 32: return by_group<DT, KT, D, 32>(p, G, st, e);
+      case 64: return by_group<DT, KT, D, 64>(p, G, st, e);
+      default: return false;
+    }
   }
 }
 
-template <int DT>
+template <int DT, int KT>
 bool by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipError_t* e) {
   switch (D) {
-    case 64: return by_block<DT, 64>(p, B, G, st, e);
-    case 128: return by_block<DT, 128>(p, B, G, st, e);
+    case 64: return by_block<DT, KT, 64>(p, B, G, st, e);
+    case 128: return by_block<DT, KT, 128>(p, B, G, st, e);
     default: return false;
   }
 }
 
 }  // namespace
 
-bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
-                           int group, hipStream_t stream, hipError_t* err) {
+bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                           int block_size, int group, hipStream_t stream, hipError_t* err) {
+  const bool fp8 = kv == PKV_FP8_E4M3;
+  if (!fp8 && kv != dt) return false;
   switch (dt) {
-    case PKV_F16: return by_dim<PKV_F16>(p, head_dim, block_size, group, stream, err);
-    case PKV_BF16: return by_dim<PKV_BF16>(p, head_dim, block_size, group, stream, err);
+    case PKV_F16:
+      return fp8 ? by_dim<PKV_F16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err)
+                 : by_dim<PKV_F16, PKV_F16>(p, head_dim, block_size, group, stream, err);
+    case PKV_BF16:
+      return fp8 ? by_dim<PKV_BF16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err)
+                 : by_dim<PKV_BF16, PKV_BF16>(p, head_dim, block_size, group, stream, err);
     default: return false;
   }
 }

@@ -51,8 +51,8 @@ struct AttnParams {
 // dt: the query / output format; kv: the caches' (dt, or PKV_FP8_E4M3).
 bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
                            int block_size, int group, hipStream_t stream, hipError_t* err);
-bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
-                           int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                           int block_size, int group, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
 
 // New tokens of a decode step (one per sequence), stored by the launch that

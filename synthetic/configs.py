@@ -87,14 +87,19 @@ CONFIGS = {
     # A sliding-window grouped-query layer (Mistral-7B-like: 32 query heads
     # over 8 KV heads, 4096-token window): only the blocks the window touches
     # hold data; table entries before them are -1.
+    6: DecodeConfig("swa_mistral7b_layer_bf16", num_seqs=64, num_q_heads=32, num_kv_heads=8,
+                    head_dim=128, dtype="bf16", block_size=16, lengths="uniform",
+                    len_lo=1024, len_hi=16384, sliding_window=4096),
     # The Llama-2-7B-shaped layer with an 8-bit E4M3 KV cache (per-tensor
     # scales 1/32; paging combined with quantization).
     8: DecodeConfig("llama2_7b_layer_fp8kv", num_seqs=64, num_q_heads=32, num_kv_heads=32,
                     head_dim=128, dtype="f16", block_size=16, lengths="uniform",
                     len_lo=128, len_hi=2048, kv_format="fp8_e4m3", k_scale=1.0 / 32, v_scale=1.0 / 32),
-    6: DecodeConfig("swa_mistral7b_layer_bf16", num_seqs=64, num_q_heads=32, num_kv_heads=8,
-                    head_dim=128, dtype="bf16", block_size=16, lengths="uniform",
-                    len_lo=1024, len_hi=16384, sliding_window=4096),
+    # The 70B-style grouped-query layer with the same 8-bit cache: quantized
+    # pages shared by 8 query heads each, on the matrix cores.
+    9: DecodeConfig("gqa70b_layer_fp8kv", num_seqs=256, num_q_heads=64, num_kv_heads=8,
+                    head_dim=128, dtype="bf16", block_size=32, lengths="uniform",
+                    len_lo=1024, len_hi=32768, kv_format="fp8_e4m3", k_scale=1.0 / 32, v_scale=1.0 / 32),
 }
 
 

@@ -158,6 +158,12 @@ def test_plan_info_reports_the_launch():
     assert info(256, 64, 8, 128, 32, 32768, 2, partition_size=512) == (512, 64, "mfma")
     assert info(256, 64, 8, 128, 32, 32768, 2, kernel="valu") == (32768, 1, "valu")
     assert info(64, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == (4112, 1, "mfma")
+    fp8 = dict(kv_format="fp8_e4m3", k_scale=1 / 32, v_scale=1 / 32)
+    assert info(256, 64, 8, 128, 32, 32768, 2, **fp8) == (32768, 1, "mfma")      # 8-bit GQA: matrix cores
+    assert info(64, 32, 32, 128, 16, 2048, 1, **fp8) == (2048, 1, "valu")        # 8-bit MHA
+    assert info(256, 64, 8, 128, 32, 32768, 2, kernel="valu", **fp8)[2] == "valu"
+    with pytest.raises(pkv.PkvError):
+        info(256, 64, 8, 128, 64, 32768, 2, kernel="mfma", **fp8)               # 8-bit: 16/32-token blocks
     part, parts, kern = info(4, 8, 8, 128, 16, 32768, 2)
     assert parts > 1 and part * parts >= 32768 and part % 16 == 0 and kern == "valu"
     assert info(64, 32, 32, 128, 16, 2048, 1, partition_size=48) == (48, 43, "valu")

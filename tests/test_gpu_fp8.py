@@ -46,24 +46,27 @@ def test_fp8_store_is_bit_exact(in_dtype, k_scale, v_scale):
 
 
 @pytest.mark.parametrize("q_dtype", ["f16", "bf16"])
-def test_every_code_decodes_exactly_through_attention(q_dtype):
+@pytest.mark.parametrize("kernel,group,B", [("valu", 2, 16), ("mfma", 4, 16), ("mfma", 16, 32)])
+def test_every_code_decodes_exactly_through_attention(q_dtype, kernel, group, B):
     """A one-token sequence returns v_scale * e4m3(code) for each code of its
-    value row: all 256 codes over 2 KV heads x 128, two query heads each."""
-    Hkv, D, B = 2, 128, 16
+    value row: all 256 codes over 2 KV heads x 128, `group` query heads
+    each, through either kernel."""
+    Hkv, D = 2, 128
     codes = np.arange(256, dtype=np.uint8).reshape(Hkv, D)
     kc = np.zeros((3, Hkv, B, D), dtype=np.uint8)
     vc = np.full((3, Hkv, B, D), 0xFF, dtype=np.uint8)
     vc[1, :, 0, :] = codes
     kc[1, :, 0, :] = 0x38                                   # key 1.0 everywhere
-    q = to_storage(np.random.default_rng(2).standard_normal((1, 2 * Hkv, D)), q_dtype)
-    say(f"fp8 decode of all codes, q {q_dtype}")
-    out = torch.empty((1, 2 * Hkv, D), dtype={"f16": torch.float16, "bf16": torch.bfloat16}[q_dtype], device="cuda")
+    q = to_storage(np.random.default_rng(2).standard_normal((1, group * Hkv, D)), q_dtype)
+    say(f"fp8 decode of all codes, q {q_dtype}, {kernel} kernel, group {group}, B {B}")
+    out = torch.empty((1, group * Hkv, D), dtype={"f16": torch.float16, "bf16": torch.bfloat16}[q_dtype],
+                      device="cuda")
     pkv.paged_attention_decode(out, to_device(q, q_dtype), to_device(kc, "fp8"), to_device(vc, "fp8"),
                                ints([[1]]), ints([1]), 0.1, B, Hkv, 1, kv_format="fp8_e4m3", k_scale=1.0,
-                               v_scale=0.5, kernel="valu")
+                               v_scale=0.5, kernel=kernel)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()[0]
-    want = np.repeat(oracle.decode_e4m3(codes) * 0.5, 2, axis=0)
+    want = np.repeat(oracle.decode_e4m3(codes) * 0.5, group, axis=0)
     assert np.array_equal(got, want, equal_nan=True)
 
 
