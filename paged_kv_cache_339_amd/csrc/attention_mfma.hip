@@ -361,10 +361,14 @@ constexpr int kMfmaWaves = PKV_MFMA_WAVES;
 #endif
 
 // Chunks loaded ahead per wave: 8-bit caches load half the bytes per chunk,
-// so two of their chunks keep the same bytes in flight as one 16-bit chunk.
+// so two of their chunks keep the same bytes in flight as one 16-bit chunk
+// (on the 8-bit GQA layer 1, 3 and 4 measured 0.6%, 3% and 1.4% slower).
+#ifndef PKV_MFMA_UNROLL_FP8
+#define PKV_MFMA_UNROLL_FP8 (2 * PKV_MFMA_UNROLL)
+#endif
 template <int KT>
 constexpr int mfma_unroll() {
-  return KT == PKV_FP8_E4M3 ? 2 * PKV_MFMA_UNROLL : PKV_MFMA_UNROLL;
+  return KT == PKV_FP8_E4M3 ? PKV_MFMA_UNROLL_FP8 : PKV_MFMA_UNROLL;
 }
 
 template <int DT, int KT, int D, int B, int G>
