@@ -63,7 +63,7 @@ class DecodeConfig:
         return replace(self, **kw)
 
 
-# The five decode workloads.  Shapes: Llama-2-7B (32 heads), Llama-2-13B
+# The decode workloads.  Shapes: Llama-2-7B (32 heads), Llama-2-13B
 # (40 heads) and a 70B-class grouped-query layer (64 query heads over 8 KV
 # heads); block size 16 is the default the glossary pages give, 32 the size
 # one of them recommends for balance.

@@ -358,3 +358,36 @@ def test_reused_work_list_across_layers_is_bit_identical(idx, partition_size):
                                    **kw)
         torch.cuda.synchronize()
         assert torch.equal(again.view(oview), ref.view(oview)), l
+
+
+LARGE_LOGIT_CASES = [
+    # dtype, Hq, Hkv, B, kernel
+    ("f32", 4, 4, 16, "valu"), ("f16", 8, 8, 16, "valu"), ("bf16", 8, 4, 32, "valu"),
+    ("bf16", 32, 8, 32, "mfma"), ("f16", 16, 4, 16, "mfma"),
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,B,kernel", LARGE_LOGIT_CASES)
+@pytest.mark.parametrize("q_gain", [8.0, 40.0])
+def test_large_logits_match_the_oracle(dtype, Hq, Hkv, B, kernel, q_gain):
+    """Queries scaled up so scores spread over hundreds (a sharply peaked
+    softmax whose running maximum jumps by large steps between blocks):
+    rows still match the oracle, with and without split-K partitions."""
+    import dataclasses
+
+    from oracle.formats import decode
+    from synthetic import to_storage
+
+    cfg = DecodeConfig(f"large_logits_{dtype}", num_seqs=5, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       dtype=dtype, block_size=B, lengths="uniform", len_lo=1, len_hi=1200)
+    lay = make_layout(cfg, seed=int(q_gain) + Hq)
+    host = host_values(lay)
+    host = dataclasses.replace(host, q=to_storage(decode(host.q, dtype) * q_gain, dtype))
+    step = DeviceStep.from_host(lay, host)
+    step.scatter()
+    want, _, _ = oracle_step(lay, host)
+    for part in (0, 8 * B):
+        say(f"large logits x{q_gain} {dtype} Hq={Hq} Hkv={Hkv} B={B} {kernel} partition={part}")
+        out = step.attend(partition_size=part, kernel=kernel)
+        torch.cuda.synchronize()
+        assert_rows_close(widen(out), want, dtype, f"large logits x{q_gain} {kernel} partition {part}")
