@@ -490,6 +490,11 @@ def main():
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="split-K partition in tokens (0 = library default; -1 = the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--placement", default=None, choices=["shuffled", "contiguous"],
+                    help="contiguous: each sequence's blocks adjacent and in order (the cost of paging)")
+    ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
+    ap.add_argument("--tp-share", type=int, default=1,
+                    help="N > 1: one GPU's share of N-way tensor parallelism (heads / N)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
@@ -517,11 +522,25 @@ def main():
         return
 
     cfg = CONFIGS[args.config]
+    part = cfg.partition_size if args.partition_size < 0 else args.partition_size
+    # The workload's name, tagged with every change from its stated form.
+    tag = cfg.name
+    if args.tp_share > 1:
+        if cfg.num_kv_heads % args.tp_share:
+            sys.exit(f"--tp-share {args.tp_share} does not divide {cfg.num_kv_heads} KV heads")
+        cfg = cfg.scaled(num_q_heads=cfg.num_q_heads // args.tp_share,
+                         num_kv_heads=cfg.num_kv_heads // args.tp_share)
+        tag += f"_tp{args.tp_share}share"
+    if args.block_size:
+        cfg = cfg.scaled(block_size=args.block_size)
+        tag += f"_b{args.block_size}"
+    if args.placement:
+        cfg = cfg.scaled(placement=args.placement)
+        tag += "" if args.placement == "shuffled" else f"_{args.placement}"
+    if part != cfg.partition_size:
+        tag += f"_partition{part or 'auto'}"
     seed = args.config if args.seed is None else args.seed
     layout = make_layout(cfg, seed=seed)
-    part = cfg.partition_size if args.partition_size < 0 else args.partition_size
-    # The workload's name, tagged when the partition differs from its stated one.
-    tag = cfg.name if part == cfg.partition_size else f"{cfg.name}_partition{part or 'auto'}"
     S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     es = DTYPE_BYTES[cfg.dtype]
     step_kv = kv_bytes(layout.context_lens, Hkv, D, cfg.kv_dtype, cfg.sliding_window)

@@ -14,17 +14,22 @@
 namespace {
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
-// Default split-K partition (tokens) when the caller asks for automatic.
-// Automatic split-K partition: the smallest power of two of at least
-// kMinAutoPartition tokens that still leaves about kFillItems
-// (sequence, KV head, partition) work items when every sequence is as long
-// as the longest.  An MI355X keeps 512 (MFMA kernel) to 1280 (vector kernel)
-// of these workgroups resident, and the plan orders them longest first, so
-// the last items are short.  Measured on the 7B/13B/GQA/sliding-window
-// layers: once there are that many items, one partition per sequence beats
-// any split (no reduce pass, no partial-result traffic), so splitting is
-// kept for batches with too few (sequence, KV head) pairs to fill the chip.
-constexpr int64_t kFillItems = 1024;
+// Automatic split-K partition.  With at least kNoSplitPairs (sequence, KV
+// head) pairs, one partition per sequence: an MI355X keeps 768 (MFMA
+// kernel) to 1280 (vector kernel) workgroups resident, the plan orders the
+// items longest first so the last ones are short, and a split would only
+// add partial results, whose writes into the saturated read stream cost far
+// more than their bytes (measured on the 7B/13B/GQA layers).  Fewer pairs
+// leave the chip underfilled: then the span is cut into equal partitions of
+// about the smallest power of two of at least kMinAutoPartition tokens that
+// gives kFillItems work items when every sequence is as long as the longest
+// (one GPU's share of the GQA layer under 4- and 8-way tensor parallelism:
+// 73% -> 78% and 71% -> 73% of peak).  A sliding window makes every long
+// sequence's span the same, so there is no long item to break up: windowed
+// batches split only below kNoSplitPairs / 4 pairs (the 512-pair
+// sliding-window layer measured ~1% slower split into five).
+constexpr int64_t kNoSplitPairs = 2048;
+constexpr int64_t kFillItems = 4096;
 constexpr int64_t kMinAutoPartition = 1024;
 
 int dtype_bytes(pkv_dtype dt) {
@@ -105,13 +110,20 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   }
   const int64_t span_tokens = span_blocks * block_size;
   if (part == 0) {
-    const int64_t want = (span_tokens * num_seqs * num_kv_heads + kFillItems - 1) / kFillItems;
-    int64_t p2 = kMinAutoPartition;
-    while (p2 < want && p2 < span_tokens) p2 <<= 1;
-    // A span just past a power of two (a window that starts inside a block)
-    // stays one partition rather than leaving a sliver for a second one.
-    if (span_tokens <= p2 + p2 / 4) p2 = span_tokens;
-    part = (int32_t)(p2 < 0x40000000 ? p2 : 0x40000000);
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    int64_t p = span_tokens;
+    if (pairs < (window > 0 ? kNoSplitPairs / 4 : kNoSplitPairs)) {
+      const int64_t want = (span_tokens * pairs + kFillItems - 1) / kFillItems;
+      int64_t p2 = kMinAutoPartition;
+      while (p2 < want && p2 < span_tokens) p2 <<= 1;
+      // A span at most a quarter past p2 stays whole; a longer one is cut
+      // into equal pieces, so no sliver of a block or two is left over.
+      if (span_tokens > p2 + p2 / 4) {
+        const int64_t n = (span_tokens + p2 - 1) / p2;
+        p = (span_tokens + n - 1) / n;
+      }
+    }
+    part = (int32_t)(p < 0x40000000 ? p : 0x40000000);
   }
   part = (int32_t)round_up(part, align);
 

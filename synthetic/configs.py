@@ -41,6 +41,7 @@ class DecodeConfig:
     kv_format: str = "same"  # "same" (caches in `dtype`) or "fp8_e4m3" (8-bit codes with scales)
     k_scale: float = 1.0
     v_scale: float = 1.0
+    placement: str = "shuffled"  # pool order: "shuffled" (seeded permutation) or "contiguous" (identity)
 
     @property
     def group(self) -> int:

@@ -4,7 +4,8 @@
 
 * the context length L of every sequence, counting the token this step
   appends (so the step writes position L-1 and then attends over L tokens);
-* the size of the physical block pool and a seeded random order of its blocks;
+* the size of the physical block pool and a seeded random order of its blocks
+  (or the identity order, for measuring what scattering the blocks costs);
 * each sequence's block table (int32, -1 padded), filled sequence by sequence
   from the front of that random order;
 * for shared-prefix workloads, the prompt blocks that the samples of one
@@ -99,6 +100,12 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
     if N < need:
         raise ValueError(f"pool of {N} blocks cannot hold {need}")
     order = rng.permutation(N)
+    if cfg.placement == "contiguous":
+        # Each sequence's blocks adjacent and in order (the permutation is
+        # still drawn, so every later draw is unchanged).
+        order = np.arange(N)
+    elif cfg.placement != "shuffled":
+        raise ValueError(f"unknown placement {cfg.placement!r}")
 
     M = max(1, max(nblk) if nblk else 1)
     tables = np.full((S, M), -1, dtype=np.int32)

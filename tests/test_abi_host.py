@@ -166,6 +166,10 @@ def test_plan_info_reports_the_launch():
         info(256, 64, 8, 128, 64, 32768, 2, kernel="mfma", **fp8)               # 8-bit: 16/32-token blocks
     part, parts, kern = info(4, 8, 8, 128, 16, 32768, 2)
     assert parts > 1 and part * parts >= 32768 and part % 16 == 0 and kern == "valu"
+    # Too few (sequence, KV head) pairs: equal partitions for ~4096 items.
+    assert info(256, 8, 1, 128, 32, 32768, 2) == (2048, 16, "mfma")             # GQA layer, TP-8 share
+    assert info(256, 16, 2, 128, 32, 32768, 2) == (4096, 8, "mfma")             # GQA layer, TP-4 share
+    assert info(16, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == (832, 5, "mfma")   # 257 blocks / 5
     assert info(64, 32, 32, 128, 16, 2048, 1, partition_size=48) == (48, 43, "valu")
     with pytest.raises(pkv.PkvError):
         info(4, 2, 2, 96, 16, 64, 0)                                             # head_dim 96
