@@ -13,7 +13,9 @@
 
 namespace {
 
-constexpr int64_t kMaxGrid = 0x7fffffff;
+// Most workgroups one launch may have: a dispatch counts work-items in 32
+// bits, and the kernels run up to 256 threads per workgroup.
+constexpr int64_t kMaxGrid = 0xffffffffll / 256;
 // Automatic split-K partition.  With at least kNoSplitPairs (sequence, KV
 // head) pairs, one partition per sequence: an MI355X keeps 768 (MFMA
 // kernel) to 1280 (vector kernel) workgroups resident, the plan orders the
@@ -381,6 +383,7 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_c
     return PKV_ERR_SHAPE;
   if (((int64_t)head_dim * es) % 16) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)num_kv_heads * head_dim * es / 16 > 0x7fffffff / 16) return PKV_ERR_SHAPE;
+  if (num_tokens > kMaxGrid) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -402,6 +405,7 @@ int pkv_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void*
   if (!good_scale(k_scale) || !good_scale(v_scale)) return PKV_ERR_SHAPE;
   if (head_dim % 16) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)num_kv_heads * head_dim / 16 > 0x7fffffff / 64) return PKV_ERR_SHAPE;
+  if (num_tokens > kMaxGrid) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))

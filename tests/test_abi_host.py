@@ -182,3 +182,16 @@ def test_plan_info_reports_the_launch():
             rows = args[0] * args[1] * parts
             want += _up(rows * args[3] * (4 if args[6] == 0 else 2)) + _up(rows * 2 * 4)
         assert pkv.workspace_bytes(*args) == want
+
+
+def test_launches_beyond_the_dispatch_limit_are_refused():
+    """A dispatch counts work-items in 32 bits: grids past 2^32 / 256
+    workgroups are shape errors, reported before anything is launched."""
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_info(70000, 8, 8, 128, 32, 32768, 1, partition_size=32)     # 70000 x 8 x 1024 workgroups
+    assert e.value.status == -2
+    assert pkv.workspace_bytes(70000, 8, 8, 128, 32, 32768, 1, partition_size=32) == 0
+    L = pkv.lib
+    st = L.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 24) + 1, 8, 128, 16, 1 << 20, 1, FAKE)
+    assert st == -2
+    assert pkv.plan_info(70000, 8, 8, 128, 32, 32768, 1)[1] == 1               # one partition: fits
