@@ -391,3 +391,46 @@ def test_large_logits_match_the_oracle(dtype, Hq, Hkv, B, kernel, q_gain):
         out = step.attend(partition_size=part, kernel=kernel)
         torch.cuda.synchronize()
         assert_rows_close(widen(out), want, dtype, f"large logits x{q_gain} {kernel} partition {part}")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,kernel", [("f16", 4, 4, "valu"), ("bf16", 16, 2, "mfma")])
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_data_errors_are_contained(dtype, Hq, Hkv, kernel, partition_size):
+    """A table entry outside the pool (or -1) inside a sequence's used range,
+    a length above max_context_len, or one past the table's capacity makes
+    that sequence's rows NaN without reading through the bad entry; every
+    other sequence still matches the oracle."""
+    B = 16
+    lens = [300, 300, 300, 300, 300, 300]
+    cfg = _edge_cfg(dtype, 128, B, Hq, Hkv).scaled(num_seqs=len(lens))
+    lay = make_layout(cfg, 11, lengths=lens)
+    host = host_values(lay)
+    step = DeviceStep.from_host(lay, host)
+    step.scatter()
+    want, _, _ = oracle_step(lay, host)
+    tables = lay.block_tables.copy()
+    tables[1, 5] = lay.num_blocks            # one past the pool
+    tables[2, 18] = -1                       # the block of the last tokens
+    tables[3, 0] = 1 << 30
+    bad_lens = lay.context_lens.copy()
+    bad_lens[4] = 301                        # above max_context_len (passed as 300)
+    bad_lens[5] = tables.shape[1] * B + 1    # past the table's capacity
+    say(f"data errors {dtype} {kernel} partition={partition_size}")
+    out = torch.empty_like(step.q)
+    pkv.paged_attention_decode(out, step.q, step.k_cache, step.v_cache, ints(tables), ints(bad_lens), cfg.scale,
+                               B, Hkv, 300, partition_size=partition_size, kernel=kernel)
+    torch.cuda.synchronize()
+    got = widen(out)
+    assert np.isnan(got[1:]).all(), "rows of sequences with data errors must be NaN"
+    assert_rows_close(got[:1], want[:1], dtype, "the valid sequence beside data errors")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,kernel", [("f16", 2, 2, "valu"), ("bf16", 16, 2, "mfma")])
+@pytest.mark.parametrize("partition_size", [0, 131072])
+def test_longest_contexts(dtype, Hq, Hkv, kernel, partition_size):
+    """Sequences of 131072 and 70001 tokens (8192-entry tables): split into
+    128 automatic partitions merged by the reduce, and unsplit, where one
+    workgroup walks its table window 128 times."""
+    cfg = _edge_cfg(dtype, 128, 16, Hq, Hkv).scaled(num_seqs=2)
+    run_case(cfg, seed=13, lengths=[131072, 70001], partition_size=partition_size, kernel=kernel,
+             label=f"long contexts {dtype} {kernel} partition={partition_size}")
