@@ -90,13 +90,16 @@ enum pkv_kernel {
 };
 
 typedef struct pkv_attn_options {
-  /* Tokens per split-K partition.  0 = automatic: the smallest power of two
-   * of at least 1024 tokens that leaves about 1024 (sequence, KV head,
-   * partition) work items if every sequence were max_context_len long (one
-   * partition when that, plus a quarter, covers the longest span).  Otherwise a
-   * positive multiple of block_size (and of 32 for the MFMA kernel).  A
-   * sequence of length L is cut into ceil(L / partition_size) partitions
-   * that separate workgroups process; a reduce kernel merges them. */
+  /* Tokens per split-K partition.  0 = automatic: one partition per sequence
+   * when there are at least 2048 (sequence, KV head) pairs (512 with a
+   * sliding window); with fewer, the longest span (max_context_len, or the
+   * window) is cut into equal partitions of about the smallest power of two
+   * of at least 1024 tokens that gives ~4096 (sequence, KV head, partition)
+   * work items, a span at most a quarter past it staying whole.
+   * pkv_paged_attention_plan_info reports the choice.  Otherwise a positive
+   * multiple of block_size (and of 32 for the MFMA kernel).  A sequence of
+   * length L is cut into ceil(L / partition_size) partitions that separate
+   * workgroups process; a reduce kernel merges them. */
   int32_t partition_size;
   int32_t kernel;            /* enum pkv_kernel */
   /* Optional hipEvent_t handles (NULL = none), recorded on the stream right
@@ -187,7 +190,8 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * Data errors are contained, never dereferenced: a table entry outside
  * [0, num_blocks), or context_lens[s] above max_context_len or
  * max_blocks_per_seq * B, makes that sequence's output rows NaN.
- * head_dim: 64 or 128.  block_size: 8, 16, 32 or 64.
+ * head_dim: 64 or 128.  block_size: 8, 16, 32 or 64 (16 or 32 with 8-bit
+ * caches).
  * workspace: device memory of at least pkv_paged_attention_workspace_bytes,
  * 16-byte aligned, required whenever num_seqs > 0; its contents need no
  * initialisation and are overwritten.  Calls that overlap in time must not
@@ -209,9 +213,12 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
  * by the same launch that builds the attention work list, then attention
  * runs as pkv_paged_attention_decode over context_lens (which count the new
  * token).  Results are bit-identical to those two calls in sequence; the
- * step saves one launch.  k_new, v_new: device [num_seqs, num_kv_heads,
- * head_dim], 16-byte aligned; slot_mapping: device int32 [num_seqs].  Other
- * arguments, workspace and errors as pkv_paged_attention_decode.
+ * step saves one launch.  With opts->reuse_plan the first launch only
+ * stores the tokens.  With an 8-bit cache format the tokens are stored as
+ * pkv_reshape_and_cache_fp8 would, with the options' scales.  k_new, v_new:
+ * device [num_seqs, num_kv_heads, head_dim] in the query format, 16-byte
+ * aligned; slot_mapping: device int32 [num_seqs].  Other arguments,
+ * workspace and errors as pkv_paged_attention_decode.
  */
 int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
                     void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
