@@ -1,0 +1,83 @@
+"""A serving loop captures its decode steps in a HIP graph (torch.cuda.graph)
+to drop per-launch host cost.  The library launches only on the stream it
+is given and sets no memory with hipMemset, so a multi-layer step (the first
+layer builds the work list, the others reuse it) replays bit-identically to
+eager execution, replay after replay."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_339_amd as pkv
+from synthetic import CONFIGS, host_values, make_layout
+from tests.gpu_util import DeviceStep, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sign_flipped(t):
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]
+    bits = {1: 0x80, 2: -0x8000, 4: -0x80000000}[t.element_size()]
+    return (t.view(view) ^ bits).view(t.dtype)
+
+
+@pytest.mark.parametrize("idx,scaled", [(2, dict(num_seqs=6)), (4, dict(num_seqs=3, partition_size=256)),
+                                        (9, dict(num_seqs=3))])
+def test_captured_multi_layer_step_replays_bit_identically(idx, scaled):
+    cfg = CONFIGS[idx].scaled(**scaled)
+    lay = make_layout(cfg, seed=90 + idx)
+    base = DeviceStep.from_host(lay, host_values(lay))
+    S, layers = len(lay.context_lens), 4
+    say(f"graph capture config {idx} S={S} layers={layers}")
+    kw = dict(partition_size=cfg.partition_size, sliding_window=cfg.sliding_window, kv_format=cfg.kv_format,
+              k_scale=cfg.k_scale, v_scale=cfg.v_scale)
+    max_ctx = max(1, lay.max_context_len)
+    ws = torch.empty(max(256, pkv.workspace_bytes(S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                                   cfg.block_size, max_ctx, pkv.ops.dtype_code(base.q),
+                                                   cfg.partition_size, "auto", cfg.sliding_window, cfg.kv_format,
+                                                   cfg.k_scale, cfg.v_scale)), dtype=torch.uint8, device="cuda")
+
+    def layer_data(l):
+        f = _sign_flipped if l % 2 else (lambda t: t)
+        return dict(q=f(base.q).clone(), kc=f(base.k_cache).clone(), vc=f(base.v_cache).clone(),
+                    kn=f(base.k_new).clone(), vn=f(base.v_new).clone(), out=torch.empty_like(base.q))
+
+    def run(data):
+        for l, d in enumerate(data):
+            pkv.decode_step(d["out"], d["q"], d["kn"], d["vn"], d["kc"], d["vc"], base.slots, base.tables,
+                            base.lens, cfg.scale, cfg.block_size, cfg.num_kv_heads, max_ctx, workspace=ws,
+                            reuse_plan=l > 0, **kw)
+
+    eager = [layer_data(l) for l in range(layers)]
+    run(eager)
+    torch.cuda.synchronize()
+
+    graph_data = [layer_data(l) for l in range(layers)]
+    pristine = [{k: v.clone() for k, v in d.items()} for d in graph_data]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):            # warm-up on a side stream, as torch asks before capture
+        run(graph_data)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(graph_data)
+    torch.cuda.synchronize()
+
+    oview = torch.int32 if cfg.dtype == "f32" else torch.int16
+    cview = {"f32": torch.int32, "fp8": torch.uint8}.get(cfg.kv_dtype, torch.int16)
+    for replay in range(3):
+        for d, p in zip(graph_data, pristine):   # caches back to their state before the step
+            d["kc"].copy_(p["kc"])
+            d["vc"].copy_(p["vc"])
+            d["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (d, e) in enumerate(zip(graph_data, eager)):
+            assert torch.equal(d["out"].view(oview), e["out"].view(oview)), (replay, l)
+            assert torch.equal(d["kc"].view(cview), e["kc"].view(cview)), (replay, l)
+            assert torch.equal(d["vc"].view(cview), e["vc"].view(cview)), (replay, l)
+        # Eager work between replays on the same tensors and workspace.
+        run(eager)
+        torch.cuda.synchronize()
