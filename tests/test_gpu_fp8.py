@@ -82,3 +82,37 @@ def test_fp8_blocks_copy_bitwise():
     oracle.copy_blocks(kc, vc, pairs)
     assert to_storage_np(dk, "fp8").tobytes() == kc.tobytes()
     assert to_storage_np(dv, "fp8").tobytes() == vc.tobytes()
+
+
+FP8_CASES = [
+    # q dtype, head_dim, block size, Hq, Hkv, kernel
+    ("f16", 64, 16, 4, 4, "valu"), ("bf16", 64, 32, 8, 4, "valu"), ("bf16", 128, 32, 2, 2, "valu"),
+    ("bf16", 64, 16, 16, 4, "mfma"), ("f16", 64, 32, 32, 4, "mfma"), ("f16", 128, 16, 16, 1, "mfma"),
+    ("bf16", 128, 32, 64, 4, "mfma"),
+]
+
+
+@pytest.mark.parametrize("q_dtype,D,B,Hq,Hkv,kernel", FP8_CASES)
+@pytest.mark.parametrize("window", [0, 300])
+def test_fp8_attention_matches_the_oracle(q_dtype, D, B, Hq, Hkv, kernel, window):
+    """8-bit caches through both kernels at head_dim 64 and 128, 16- and
+    32-token blocks, group sizes 1-16, with and without a sliding window
+    and split-K: every row against the oracle (same stored codes)."""
+    from synthetic import DecodeConfig, host_values, make_layout
+    from tests.gpu_util import DeviceStep, assert_rows_close, oracle_step, widen
+
+    lens = [1, B - 1, B + 1, 77, 300, 301, 640, 1000]
+    cfg = DecodeConfig(f"fp8_{q_dtype}_{D}", num_seqs=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       dtype=q_dtype, block_size=B, lengths="fixed", fixed_lengths=(1,), pool_factor=1.5,
+                       sliding_window=window, kv_format="fp8_e4m3", k_scale=1.0 / 16, v_scale=1.0 / 8)
+    lay = make_layout(cfg, 21, lengths=lens)
+    host = host_values(lay)
+    step = DeviceStep.from_host(lay, host)
+    step.scatter()
+    want, kc, vc = oracle_step(lay, host)
+    assert to_storage_np(step.k_cache, "fp8").tobytes() == kc.tobytes()
+    for part in (0, 128):
+        say(f"fp8 attention {q_dtype} D{D} B{B} G{Hq // Hkv} {kernel} window={window} partition={part}")
+        out = step.attend(partition_size=part, kernel=kernel)
+        torch.cuda.synchronize()
+        assert_rows_close(widen(out), want, q_dtype, f"fp8 {q_dtype} D{D} B{B} {kernel} w{window} p{part}")
