@@ -320,11 +320,12 @@ def beam_bench(args):
     real search reads the step's scores before choosing parents)."""
     import torch
     import paged_kv_cache_339_amd as pkv
-    from paged_kv_cache_339_amd._lib import AttnOptions, lib
+    from paged_kv_cache_339_amd._lib import CACHE_POLICIES, AttnOptions, lib
     from paged_kv_cache_339_amd.ops import dtype_code
 
     K, W = args.steps, args.warmup
     base = BEAM_CONFIGS[args.config]
+    policy = args.cache_policy or base.cache_policy
     cfg = base.scaled(steps=max(base.steps, K + W))
     seed = args.config if args.seed is None else args.seed
     R, Wb, B, Hq, Hkv, D = cfg.num_requests, cfg.beam_width, cfg.block_size, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
@@ -391,7 +392,7 @@ def beam_bench(args):
             st = lib.pkv_copy_blocks(vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["pairs"].data_ptr()), n_pairs,
                                      Hkv, B, D, N, code, vp(stream.cuda_stream))
             assert st == 0, st
-        opts = AttnOptions(0, 0, begins[t], ends[t], 0)
+        opts = AttnOptions(0, 0, begins[t], ends[t], 0, 0, 1.0, 1.0, 0, CACHE_POLICIES[policy])
         st = lib.pkv_decode_step(vp(out.data_ptr()), vp(qs[t].data_ptr()), vp(ks[t].data_ptr()), vp(vs[t].data_ptr()),
                                  vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["slots"].data_ptr()),
                                  vp(dbuf["tables"].data_ptr()), vp(dbuf["lens"].data_ptr()), cfg.scale, B, Hkv, S,
@@ -422,7 +423,8 @@ def beam_bench(args):
         "metric": METRIC, "value": round(kv / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "requests": R, "beam_width": Wb, "prompt_len": cfg.prompt_len,
+        "config": {"workload": cfg.name + ("" if policy == base.cache_policy else f"_{policy}"),
+                   "cache_policy": policy, "requests": R, "beam_width": Wb, "prompt_len": cfg.prompt_len,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B, "kv_dtype": cfg.dtype,
                    "pool_blocks": N, "kv_bytes_per_step": int(kv),
                    "step": "host fork/free/append + H2D tables + copy_blocks + decode_step + sync"},
@@ -495,6 +497,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
     ap.add_argument("--tp-share", type=int, default=1,
                     help="N > 1: one GPU's share of N-way tensor parallelism (heads / N)")
+    ap.add_argument("--cache-policy", default=None, choices=["stream", "keep"],
+                    help="override the workload's key/value load policy")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
@@ -537,6 +541,9 @@ def main():
     if args.placement:
         cfg = cfg.scaled(placement=args.placement)
         tag += "" if args.placement == "shuffled" else f"_{args.placement}"
+    if args.cache_policy and args.cache_policy != cfg.cache_policy:
+        cfg = cfg.scaled(cache_policy=args.cache_policy)
+        tag += f"_{args.cache_policy}"
     if part != cfg.partition_size:
         tag += f"_partition{part or 'auto'}"
     seed = args.config if args.seed is None else args.seed
@@ -555,7 +562,7 @@ def main():
 
     import torch
     import paged_kv_cache_339_amd as pkv
-    from paged_kv_cache_339_amd._lib import KERNELS, KV_FORMATS, AttnOptions, lib
+    from paged_kv_cache_339_amd._lib import CACHE_POLICIES, KERNELS, KV_FORMATS, AttnOptions, lib
     from paged_kv_cache_339_amd.ops import dtype_code
     from synthetic import device_values
 
@@ -609,7 +616,8 @@ def main():
     kvf = KV_FORMATS[cfg.kv_format]
     chosen_part, parts_per_seq, kernel_used = pkv.plan_info(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, win,
                                                             cfg.kv_format, cfg.k_scale, cfg.v_scale)
-    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 0)
+    cp = CACHE_POLICIES[cfg.cache_policy]
+    plain = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 0, cp)
     warm_args = step_args(plain)
 
     def step(a):
@@ -640,7 +648,7 @@ def main():
     # workspace (reuse_plan), between two events; with one, events go right
     # before and after the main kernel inside each of K more steps.
     if parts_per_seq == 1:
-        reuse = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 1)
+        reuse = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 1, cp)
         dec = decode_args(reuse)
         m0, m1 = ev.create(), ev.create()
         ev.record(m0, stream)
@@ -656,7 +664,7 @@ def main():
         ends = [ev.create() for _ in range(K)]
         for i in range(K):
             step(step_args(AttnOptions(part, KERNELS[args.kernel], begins[i], ends[i], win, kvf, cfg.k_scale,
-                                       cfg.v_scale, 0)))
+                                       cfg.v_scale, 0, cp)))
         torch.cuda.synchronize()
         main_ms = [ev.ms(begins[i], ends[i]) for i in range(K)]
         main_timing = "events right before and after the main kernel in each of K steps"
@@ -691,7 +699,7 @@ def main():
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
             "kv_bytes_per_step": step_kv, "partition_size": part, "partition_tokens": chosen_part,
             "partitions_per_seq": parts_per_seq, "kernel": kernel_used,
-            "sliding_window": win, "kv_format": cfg.kv_format,
+            "sliding_window": win, "kv_format": cfg.kv_format, "cache_policy": cfg.cache_policy,
             "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
         },
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),

@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 KV_FORMATS = {"same": 0, "fp8_e4m3": 1}
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+CACHE_POLICIES = {"stream": 0, "keep": 1}
 
 c_i32, c_f32, c_size, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -17,7 +18,8 @@ c_i32p = ctypes.POINTER(ctypes.c_int32)
 class AttnOptions(ctypes.Structure):
     _fields_ = [("partition_size", c_i32), ("kernel", c_i32),
                 ("main_begin_event", c_vp), ("main_end_event", c_vp), ("sliding_window", c_i32),
-                ("kv_format", c_i32), ("k_scale", c_f32), ("v_scale", c_f32), ("reuse_plan", c_i32)]
+                ("kv_format", c_i32), ("k_scale", c_f32), ("v_scale", c_f32), ("reuse_plan", c_i32),
+                ("cache_policy", c_i32)]
 
 
 class PkvError(RuntimeError):

@@ -54,6 +54,7 @@ bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 struct Plan {
   int kernel;
   bool fp8;
+  bool keep;          // plain key/value loads (PKV_CACHE_KEEP)
   int32_t window;
   int32_t part_blocks;
   int32_t max_parts;
@@ -72,6 +73,9 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   if (dtype_bytes(dtype) == 0 || dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
     return PKV_ERR_SHAPE;
+  const int32_t cache_policy = opts ? opts->cache_policy : PKV_CACHE_STREAM;
+  if (cache_policy != PKV_CACHE_STREAM && cache_policy != PKV_CACHE_KEEP) return PKV_ERR_SHAPE;
+  plan->keep = cache_policy == PKV_CACHE_KEEP;
   const int32_t kv_format = opts ? opts->kv_format : PKV_KV_SAME;
   if (kv_format != PKV_KV_SAME && kv_format != PKV_KV_FP8_E4M3) return PKV_ERR_DTYPE;
   const bool fp8 = kv_format == PKV_KV_FP8_E4M3;
@@ -299,9 +303,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   }
   const bool have = plan.kernel == PKV_KERNEL_MFMA
                         ? pkv::launch_attention_mfma(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, group, s, &err)
+                                                     head_dim, block_size, group, plan.keep, s, &err)
                         : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, group, s, &err);
+                                                     head_dim, block_size, group, plan.keep, s, &err);
   if (!have) return PKV_ERR_UNSUPPORTED;
   if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_end_event) {

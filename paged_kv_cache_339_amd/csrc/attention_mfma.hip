@@ -1,437 +1,19 @@
-// Paged decode attention for grouped-query heads on the matrix cores.
-//
-// When G query heads share one KV head (heads sharing one set of keys and
-// values, systemdesign.academy glossary "Paged Attention"), each key/value
-// tile is used G times, and the two products per 32-token chunk are small
-// dense contractions:
-//     scores^T [32 tok x 16]  = K [32 tok x D] * Q^T [D x 16]
-//     out^T    [D x 16]      += V^T [D x 32 tok] * P^T [32 tok x 16]
-// with the G heads padded to the 16 columns of v_mfma_f32_16x16x32_{bf16,f16}
-// (fp32 accumulate).  Keys and values are still read once, through the
-// block table, exactly as in the vector-ALU kernel; the workgroup layout
-// (sequence, KV head, split-K partition) and the epilogue are shared.
-//
-// Operand layouts of the 16x16x32 MFMA (lane l, r = l % 16, q = l / 16):
-//   A (16 x 32): lane holds A[r][8q .. 8q+7]
-//   B (32 x 16): lane holds B[8q .. 8q+7][r]
-//   C (16 x 16): lane holds C[4q + i][r], i = 0..3
-// The contraction index of a product may be permuted freely as long as A
-// and B agree, and so may the rows of A; both freedoms are used so that
-// every lane loads whole 16-byte runs and no data crosses lanes:
-//  * score product: A row R of output tile t is token 8(R/4) + 4t + R%4 and
-//    the contraction index k of k-step s is element 32s + k of head_dim;
-//    lane (r, q) thus ends up with the scores of head r for the eight
-//    consecutive tokens 8q .. 8q+7 of the chunk.
-//  * value product: lane (r, q) loads tokens 8q .. 8q+7, elements
-//    [DPL r, DPL r + DPL) of head_dim (DPL = D/16); an 8x8 transpose of
-//    16-bit values inside the lane (v_perm_b32) gives, for each n < DPL, the
-//    A operand row "element DPL r + n over those tokens"; the B operand is
-//    the lane's own eight softmax weights.  Output tile n then holds, in
-//    lane (r, q), head r at elements DPL(4q + i) + n.
-//
-// 8-bit (E4M3) caches: codes are decoded to the query's 16-bit format in
-// registers (v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1, exact for every
-// code; checked on all 256) and go through the same MFMA.  A lane's 16-byte
-// load of a key row then holds 16 codes, elements 64c + 16q .. +16: the
-// first eight feed k-step 2c, the last eight k-step 2c + 1, and the query
-// operand is read in that order.  The key scale is folded into the softmax
-// scale, the value scale into the output.
-#include "attention_common.h"
+// Matrix-core decode attention for grouped-query heads
+// (attention_mfma_impl.h), instances whose key and value loads carry the
+// nontemporal hint: caches streamed once per step.
+#include "attention_mfma_impl.h"
 
 namespace pkv {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-template <int DT> struct Mfma;
-
-template <> struct Mfma<PKV_BF16> {
-  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
-                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_bf16(x); }
-};
-
-template <> struct Mfma<PKV_F16> {
-  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
-                                                  __builtin_bit_cast(v8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_f16(x); }
-};
-
-// Four E4M3 codes (one dword) -> four 16-bit values of format DT (two dwords).
-template <int DT>
-__device__ __forceinline__ u32x2 decode4_e4m3(uint32_t w) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  if constexpr (DT == PKV_BF16) {
-    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
-  } else {
-    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true))};
-  }
+bool launch_attention_mfma_stream(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                                  int block_size, int group, hipStream_t stream, hipError_t* err) {
+  return mfma_dispatch<true>(p, dt, kv, head_dim, block_size, group, stream, err);
 }
-
-// Eight codes (two dwords) -> one 16-bit MFMA operand register group.
-template <int DT>
-__device__ __forceinline__ u32x4 decode8_e4m3(uint32_t w0, uint32_t w1) {
-  const u32x2 a = decode4_e4m3<DT>(w0), b = decode4_e4m3<DT>(w1);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
-template <int DPL> struct VRow;
-template <> struct VRow<8> {
-  typedef u32x4 type;
-  static __device__ __forceinline__ type load(const char* p) { return load16_kv(p); }
-  static __device__ __forceinline__ type zero() { return u32x4{0, 0, 0, 0}; }
-};
-template <> struct VRow<4> {
-  typedef u32x2 type;
-  static __device__ __forceinline__ type load(const char* p) {
-    if constexpr (PKV_NT_KV) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    return *reinterpret_cast<const u32x2*>(p);
-  }
-  static __device__ __forceinline__ type zero() { return u32x2{0, 0}; }
-};
-
-// A lane's DPL value elements of one token, as loaded (KT) and as the
-// 16-bit operand the transpose works on.
-template <int DT, int KT, int DPL> struct VLoad;
-template <int DT, int DPL> struct VLoad<DT, DT, DPL> {
-  typedef typename VRow<DPL>::type raw;
-  static __device__ __forceinline__ raw load(const char* p) { return VRow<DPL>::load(p); }
-  static __device__ __forceinline__ raw zero() { return VRow<DPL>::zero(); }
-  static __device__ __forceinline__ typename VRow<DPL>::type widen(raw x) { return x; }
-};
-template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 8> {
-  typedef u32x2 raw;
-  static __device__ __forceinline__ raw load(const char* p) { return VRow<4>::load(p); }
-  static __device__ __forceinline__ raw zero() { return u32x2{0, 0}; }
-  static __device__ __forceinline__ u32x4 widen(raw x) { return decode8_e4m3<DT>(x[0], x[1]); }
-};
-template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 4> {
-  typedef uint32_t raw;
-  static __device__ __forceinline__ raw load(const char* p) {
-    if constexpr (PKV_NT_KV) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-    return *reinterpret_cast<const uint32_t*>(p);
-  }
-  static __device__ __forceinline__ raw zero() { return 0u; }
-  static __device__ __forceinline__ u32x2 widen(raw x) { return decode4_e4m3<DT>(x); }
-};
-
-// Waves per SIMD the register allocation must allow.  3 (168 registers,
-// no spills) helps only when partitions are short; with the default
-// partitions 2 measured up to 3% faster.
-#ifndef PKV_MFMA_OCC
-#define PKV_MFMA_OCC 2
-#endif
-
-template <int DT, int KT, int D, int B, int G, int NW, int U>
-__global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(AttnParams p) {
-  constexpr int ES = 2;           // query / operand bytes per element
-  constexpr bool F8 = KT == PKV_FP8_E4M3;
-  constexpr int KES = F8 ? 1 : 2; // cache bytes per element
-  constexpr int KS = D / 32;      // k-steps of the score product
-  constexpr int KL = F8 ? KS / 2 : KS;   // 16-byte key loads per token row and lane
-  constexpr int DPL = D / 16;     // value elements per lane per token
-  constexpr int CH = 32;          // tokens per chunk
-  static_assert(G >= 1 && G <= 16, "query group must fit 16 MFMA columns");
-  static_assert(B >= 8, "8 consecutive tokens of a lane must share a block");
-  using Ops = Mfma<DT>;
-  using VL = VLoad<DT, KT, DPL>;
-
-  __shared__ MergeSmem<D, G, NW> sm;
-
-  const WorkItem it = work_item(p);
-  if (!it.valid) return;
-  const int lane = lane_id(), w = wave_id();
-
-  // Table entries of a 64-block window of the partition, one per lane; a
-  // token's block is then a lane shuffle away.  The first window is fetched
-  // before the sequence length arrives (it lies inside the row whatever the
-  // length, and is exact unless a sliding window starts the partition later),
-  // so the two loads overlap.
-  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
-  const int b0_guess = it.part * p.part_blocks;
-  int tab = b0_guess + lane < p.max_blocks_per_seq ? table[b0_guess + lane] : -1;
-
-  // Query rows of the G heads (the B operand of the score product), also
-  // fetched before the length.
-  const int r = lane & 15, q = lane >> 4;
-  u32x4 qb[KS];
-  {
-    const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // Element offset of k-step ks past 8q: 32 ks, or for 8-bit caches
-      // 64 (ks / 2) + 8 q + 8 (ks % 2) (the order the key loads give).
-      const int off = F8 ? 64 * (ks / 2) + 8 * q + 8 * (ks % 2) : 32 * ks;
-      qb[ks] = (r < G) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
-    }
-  }
-
-  const SeqWork sw = seq_work(p, it.s, B);
-  if (sw.bad) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
-    return;
-  }
-  if (sw.L == 0) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, 0.f);
-    return;
-  }
-  if (it.part >= sw.nparts) return;
-
-  const int Hkv = p.num_kv_heads, L = sw.L, t0 = sw.t0, N = p.num_blocks;
-
-  f32x4 o[DPL];
-#pragma unroll
-  for (int n = 0; n < DPL; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-  int bad = 0;
-
-  const char* kbase = reinterpret_cast<const char*>(p.k_cache);
-  const char* vbase = reinterpret_cast<const char*>(p.v_cache);
-  // Chunks start on a block boundary (the block of t0 for the first
-  // partition), so every token at or after tb lies in a block the table
-  // maps; tokens before t0 are masked like tokens past L.
-  const int pb0 = sw.blk0 + it.part * p.part_blocks;             // first block of the partition
-  const int pb1 = min(sw.blk0 + sw.nblk, pb0 + p.part_blocks);   // one past its last block
-  const int tb = pb0 * B;
-  const int te = min(L, tb + p.part_blocks * B);
-  const int nch = (te - tb + CH - 1) / CH;
-
-  // The table window moves forward when a chunk reaches past it
-  // (wave-uniform).  Entries past pb1 are never used.
-  int tab_base = pb0;
-  if (pb0 != b0_guess) tab = pb0 + lane < pb1 ? table[pb0 + lane] : -1;
-
-  // Wave w takes U consecutive chunks at a time; the key and value loads of
-  // all U are issued before the first is used.
-  for (int cu = w * U; cu < nch; cu += NW * U) {
-    const int c00 = tb + cu * CH;
-    if (min(pb1 - 1, (c00 + U * CH - 1) / B) >= tab_base + kWave) {
-      tab_base = c00 / B;
-      tab = tab_base + lane < pb1 ? table[tab_base + lane] : -1;
-    }
-
-    // Keys: lane (r, q) loads token 8(r/4) + 4t + r%4 of the chunk for t = 0, 1,
-    // head_dim elements 32s + 8q .. +8 for every k-step s (8-bit caches:
-    // elements 64c + 16q .. +16 for k-steps 2c and 2c + 1).
-    u32x4 kr[U][2][KL];
-    // Values: tokens 8q .. 8q+7 (one block), elements DPL r .. DPL r + DPL.
-    typename VL::raw vr[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // A chunk at or past te (the last group of a partition) loads nothing;
-      // te is L or a 32-token-aligned partition end, so no chunk straddles it.
-      const int c0 = c00 + u * CH;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int tok = c0 + 8 * (r >> 2) + 4 * t + (r & 3);
-        bool ok = tok < te && tok >= t0;
-        int blk = __shfl(tab, min(tok / B - tab_base, kWave - 1), kWave);
-        if (ok && (unsigned)blk >= (unsigned)N) {
-          bad = 1;
-          ok = false;
-        }
-        const char* kp = kbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tok % B) * D +
-                                  (F8 ? 16 : 8) * q) * KES;
-#pragma unroll
-        for (int kl = 0; kl < KL; ++kl)
-          kr[u][t][kl] = ok ? load16_kv(kp + (F8 ? 64 : 32) * kl * KES) : u32x4{0, 0, 0, 0};
-      }
-      const int tv0 = c0 + 8 * q;
-      bool ok = tv0 < te && tv0 + 7 >= t0;
-      int blk = __shfl(tab, min(tv0 / B - tab_base, kWave - 1), kWave);
-      if (ok && (unsigned)blk >= (unsigned)N) {
-        bad = 1;
-        ok = false;
-      }
-      const char* vp = vbase + ((((size_t)(ok ? blk : 0) * Hkv + it.h) * B + tv0 % B) * D + DPL * r) * KES;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        vr[u][j] = (ok && tv0 + j < te && tv0 + j >= t0) ? VL::load(vp + (size_t)j * D * KES) : VL::zero();
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c0 = c00 + u * CH;
-      if (c0 >= te) break;
-      // Scores of head r for tokens c0 + 8q + j, j = 4t + i.
-      float sc[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 a;
-          if constexpr (F8) {
-            const u32x4 w = kr[u][t][ks / 2];
-            a = (ks % 2) ? decode8_e4m3<DT>(w[2], w[3]) : decode8_e4m3<DT>(w[0], w[1]);
-          } else {
-            a = kr[u][t][ks];
-          }
-          acc = Ops::mma(a, qb[ks], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i] * p.scale_log2;
-      }
-      if (c0 + CH > L || c0 < t0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c0 + 8 * q + j >= L || c0 + 8 * q + j < t0) sc[j] = -INFINITY;
-      }
-
-      float cm = sc[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
-      cm = fmaxf(cm, shfl_xor_f(cm, 16));
-      cm = fmaxf(cm, shfl_xor_f(cm, 32));
-      const float mn = fmaxf(m, cm);
-      const float ref = softmax_ref(mn);
-      const float alpha = fast_exp2(m - ref);
-      m = mn;
-
-      // Weights rounded to the operand format; the sum uses the rounded values.
-      u32x4 pb;
-      float ps = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = Ops::narrow(fast_exp2(sc[2 * k] - ref));
-        const uint32_t hi = Ops::narrow(fast_exp2(sc[2 * k + 1] - ref));
-        pb[k] = lo | (hi << 16);
-        ps += widen_half<DT>(pb[k], false) + widen_half<DT>(pb[k], true);
-      }
-      l = fmaf(l, alpha, ps);
-
-      typename VRow<DPL>::type v16[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v16[j] = VL::widen(vr[u][j]);
-#pragma unroll
-      for (int n = 0; n < DPL; ++n) {
-        u32x4 a;
-        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          a[k] = __builtin_amdgcn_perm(v16[2 * k + 1][n >> 1], v16[2 * k][n >> 1], sel);
-        o[n] *= alpha;
-        o[n] = Ops::mma(a, pb, o[n]);
-      }
-    }
-  }
-
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
-  const int any_bad = __any(bad);
-
-  if (r < G) {
-#pragma unroll
-    for (int n = 0; n < DPL; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.o[w][r][DPL * (4 * q + i) + n] = o[n][i];
-    if (q == 0) {
-      sm.m[w][r] = m;
-      sm.l[w][r] = l;
-    }
-  }
-  if (lane == 0) sm.bad[w] = any_bad;
-  __syncthreads();
-  merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
-}
-
-// ---------------------------------------------------------------------------
-namespace {
-
-// Waves per workgroup.  1 and 2 measured no faster with 512-token
-// partitions and slower with long ones.
-#ifndef PKV_MFMA_WAVES
-#define PKV_MFMA_WAVES 4
-#endif
-constexpr int kMfmaWaves = PKV_MFMA_WAVES;
-// 32-token chunks a wave loads ahead.  2 (204 VGPRs, still 2 waves per
-// SIMD) measured within +-4% of 1 across the GQA and sliding-window layers.
-#ifndef PKV_MFMA_UNROLL
-#define PKV_MFMA_UNROLL 1
-#endif
-
-// Chunks loaded ahead per wave: 8-bit caches load half the bytes per chunk,
-// so two of their chunks keep the same bytes in flight as one 16-bit chunk
-// (on the 8-bit GQA layer 1, 3 and 4 measured 0.6%, 3% and 1.4% slower).
-#ifndef PKV_MFMA_UNROLL_FP8
-#define PKV_MFMA_UNROLL_FP8 (2 * PKV_MFMA_UNROLL)
-#endif
-template <int KT>
-constexpr int mfma_unroll() {
-  return KT == PKV_FP8_E4M3 ? PKV_MFMA_UNROLL_FP8 : PKV_MFMA_UNROLL;
-}
-
-template <int DT, int KT, int D, int B, int G>
-hipError_t launch_mfma(const AttnParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
-  hipLaunchKernelGGL((attn_mfma_kernel<DT, KT, D, B, G, kMfmaWaves, mfma_unroll<KT>()>), grid,
-                     dim3(kMfmaWaves * kWave), 0, st, p);
-  return hipGetLastError();
-}
-
-template <int DT, int KT, int D, int B>
-bool by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
-  switch (G) {
-    case 4: *e = launch_mfma<DT, KT, D, B, 4>(p, st); return true;
-    case 8: *e = launch_mfma<DT, KT, D, B, 8>(p, st); return true;
-    case 16: *e = launch_mfma<DT, KT, D, B, 16>(p, st); return true;
-    default: return false;
-  }
-}
-
-template <int DT, int KT, int D>
-bool by_block(const AttnParams& p, int B, int G, hipStream_t st, hipError_t* e) {
-  if constexpr (KT == PKV_FP8_E4M3) {
-    switch (B) {                      // 8-bit caches: 16- and 32-token blocks
-      case 16: return by_group<DT, KT, D, 16>(p, G, st, e);
-      case 32: return by_group<DT, KT, D, 32>(p, G, st, e);
-      default: return false;
-    }
-  } else {
-    switch (B) {
-      case 8: return by_group<DT, KT, D, 8>(p, G, st, e);
-      case 16: return by_group<DT, KT, D, 16>(p, G, st, e);
-      case 32: return by_group<DT, KT, D, 32>(p, G, st, e);
-      case 64: return by_group<DT, KT, D, 64>(p, G, st, e);
-      default: return false;
-    }
-  }
-}
-
-template <int DT, int KT>
-bool by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipError_t* e) {
-  switch (D) {
-    case 64: return by_block<DT, KT, 64>(p, B, G, st, e);
-    case 128: return by_block<DT, KT, 128>(p, B, G, st, e);
-    default: return false;
-  }
-}
-
-}  // namespace
 
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                           int block_size, int group, hipStream_t stream, hipError_t* err) {
-  const bool fp8 = kv == PKV_FP8_E4M3;
-  if (!fp8 && kv != dt) return false;
-  switch (dt) {
-    case PKV_F16:
-      return fp8 ? by_dim<PKV_F16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err)
-                 : by_dim<PKV_F16, PKV_F16>(p, head_dim, block_size, group, stream, err);
-    case PKV_BF16:
-      return fp8 ? by_dim<PKV_BF16, PKV_FP8_E4M3>(p, head_dim, block_size, group, stream, err)
-                 : by_dim<PKV_BF16, PKV_BF16>(p, head_dim, block_size, group, stream, err);
-    default: return false;
-  }
+                           int block_size, int group, bool keep, hipStream_t stream, hipError_t* err) {
+  return keep ? launch_attention_mfma_keep(p, dt, kv, head_dim, block_size, group, stream, err)
+              : launch_attention_mfma_stream(p, dt, kv, head_dim, block_size, group, stream, err);
 }
 
 }  // namespace pkv

@@ -48,11 +48,22 @@ struct AttnParams {
 };
 
 // Returns false when no kernel instance exists for the combination.
-// dt: the query / output format; kv: the caches' (dt, or PKV_FP8_E4M3).
+// dt: the query / output format; kv: the caches' (dt, or PKV_FP8_E4M3);
+// keep: plain key/value loads (blocks shared across the batch are served
+// again from cache) instead of nontemporal ones.
 bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                           int block_size, int group, hipStream_t stream, hipError_t* err);
+                           int block_size, int group, bool keep, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                           int block_size, int group, hipStream_t stream, hipError_t* err);
+                           int block_size, int group, bool keep, hipStream_t stream, hipError_t* err);
+// The two load policies' instances, each built in a translation unit of its own.
+bool launch_attention_valu_stream(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                                  int block_size, int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_valu_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                                int block_size, int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_mfma_stream(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                                  int block_size, int group, hipStream_t stream, hipError_t* err);
+bool launch_attention_mfma_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
+                                int block_size, int group, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
 
 // New tokens of a decode step (one per sequence), stored by the launch that

@@ -10,7 +10,7 @@ import ctypes
 
 import numpy as np
 
-from ._lib import KERNELS, KV_FORMATS, AttnOptions, PkvError, c_i32p, check, lib
+from ._lib import CACHE_POLICIES, KERNELS, KV_FORMATS, AttnOptions, PkvError, c_i32p, check, lib
 
 
 def _torch():
@@ -50,12 +50,13 @@ def _dev(t, name, dtype=None, ndim=None):
 
 
 def _options(partition_size, kernel, main_events, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,
-             reuse_plan=False):
+             reuse_plan=False, cache_policy="stream"):
     ev0, ev1 = (None, None) if main_events is None else main_events
     return AttnOptions(int(partition_size), KERNELS[kernel],
                        None if ev0 is None else ctypes.c_void_p(int(ev0)),
                        None if ev1 is None else ctypes.c_void_p(int(ev1)), int(sliding_window),
-                       KV_FORMATS[kv_format], float(k_scale), float(v_scale), int(bool(reuse_plan)))
+                       KV_FORMATS[kv_format], float(k_scale), float(v_scale), int(bool(reuse_plan)),
+                       CACHE_POLICIES[cache_policy])
 
 
 def plan_info(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, dtype_code_,
@@ -116,14 +117,16 @@ def _ws_args(workspace):
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, max_context_len, partition_size=0, kernel="auto",
                            workspace=None, stream=None, main_events=None, sliding_window=0, kv_format="same",
-                           k_scale=1.0, v_scale=1.0, reuse_plan=False):
+                           k_scale=1.0, v_scale=1.0, reuse_plan=False, cache_policy="stream"):
     """out[s, j] = softmax(scale * q[s, j] K_s^T) V_s through the block tables.
 
     q, out: [S, Hq, D]; k_cache, v_cache: [N, Hkv, B, D]; block_tables int32
     [S, M]; context_lens int32 [S] (device); max_context_len: host int >=
     every context length.  `workspace`: optional uint8 device tensor of at
     least workspace_bytes(...) bytes.  reuse_plan: the workspace holds the
-    work list of an earlier call with the same batch (see pkv.h)."""
+    work list of an earlier call with the same batch (see pkv.h).
+    cache_policy: "stream" (nontemporal loads) or "keep" (plain loads, for
+    batches whose sequences share blocks)."""
     if reuse_plan and workspace is None:
         raise ValueError("reuse_plan needs the workspace of the call that built the work list")
     torch = _torch()
@@ -134,7 +137,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
                            sliding_window, kv_format, k_scale, v_scale)
-    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan,
+                    cache_policy)
     st = lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
@@ -147,7 +151,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
 def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
                 block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
                 stream=None, main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,
-                reuse_plan=False):
+                reuse_plan=False, cache_policy="stream"):
     """reshape_and_cache(k_new, v_new, ..., slot_mapping) followed by
     paged_attention_decode(...), with the token store and the attention work
     list in one launch.  k_new, v_new: [S, Hkv, D]; slot_mapping int32 [S]."""
@@ -167,7 +171,8 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
                            sliding_window, kv_format, k_scale, v_scale)
-    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan,
+                    cache_policy)
     st = lib.pkv_decode_step(
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32),

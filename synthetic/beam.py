@@ -27,6 +27,7 @@ class BeamConfig:
     dtype: str
     block_size: int
     pool_factor: float = 1.25
+    cache_policy: str = "keep"   # the beams of a request share their prompt blocks
 
     @property
     def num_seqs(self) -> int:

@@ -42,6 +42,7 @@ class DecodeConfig:
     k_scale: float = 1.0
     v_scale: float = 1.0
     placement: str = "shuffled"  # pool order: "shuffled" (seeded permutation) or "contiguous" (identity)
+    cache_policy: str = "stream"  # attention loads: "stream" (nontemporal) or "keep" (shared blocks re-read)
 
     @property
     def group(self) -> int:
@@ -84,7 +85,7 @@ CONFIGS = {
     5: DecodeConfig("shared_prefix_sampling_bf16", num_seqs=512, num_q_heads=40, num_kv_heads=40,
                     head_dim=128, dtype="bf16", block_size=16, lengths="shared_prefix",
                     len_lo=1, len_hi=512, prompt_len=1000, samples_per_prompt=8,
-                    partition_size=1024),
+                    partition_size=1024, cache_policy="keep"),
     # A sliding-window grouped-query layer (Mistral-7B-like: 32 query heads
     # over 8 KV heads, 4096-token window): only the blocks the window touches
     # hold data; table entries before them are -1.

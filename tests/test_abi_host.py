@@ -195,3 +195,15 @@ def test_launches_beyond_the_dispatch_limit_are_refused():
     st = L.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, (1 << 24) + 1, 8, 128, 16, 1 << 20, 1, FAKE)
     assert st == -2
     assert pkv.plan_info(70000, 8, 8, 128, 32, 32768, 1)[1] == 1               # one partition: fits
+
+
+def test_cache_policy_values():
+    """Both load policies plan the same launch; any other value is refused."""
+    sizes = []
+    for policy in (0, 1, 2, -1):
+        opts = AttnOptions(0, 0, None, None, 0, 0, 1.0, 1.0, 0, policy)
+        sizes.append(pkv.lib.pkv_paged_attention_workspace_bytes(64, 32, 8, 128, 16, 4096, 2, ctypes.byref(opts)))
+        st = pkv.lib.pkv_paged_attention_plan_info(64, 32, 8, 128, 16, 4096, 2, ctypes.byref(opts), None, None,
+                                                   None)
+        assert st == (0 if policy in (0, 1) else -2), policy
+    assert sizes[0] == sizes[1] > 0 and sizes[2] == sizes[3] == 0

@@ -434,3 +434,20 @@ def test_longest_contexts(dtype, Hq, Hkv, kernel, partition_size):
     cfg = _edge_cfg(dtype, 128, 16, Hq, Hkv).scaled(num_seqs=2)
     run_case(cfg, seed=13, lengths=[131072, 70001], partition_size=partition_size, kernel=kernel,
              label=f"long contexts {dtype} {kernel} partition={partition_size}")
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5, 6, 8, 9])
+def test_cache_policies_give_identical_bits(idx):
+    """Streaming (nontemporal) and keeping (plain) key/value loads differ in
+    speed only: both kernels, 16- and 8-bit caches, a window, split-K."""
+    cfg = CONFIGS[idx].scaled(**SCALED[idx])
+    lay = make_layout(cfg, seed=80 + idx)
+    step = DeviceStep.from_host(lay, host_values(lay))
+    step.scatter()
+    view = torch.int32 if cfg.dtype == "f32" else torch.int16
+    for part in (0, 128):
+        say(f"cache policies config {idx} partition={part}")
+        a = step.attend(partition_size=part, cache_policy="stream").clone()
+        b = step.attend(partition_size=part, cache_policy="keep").clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(view), b.view(view)), part
