@@ -511,7 +511,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
             "(the decode step shards by KV head or by sequence with no exchange); run with --gpus 1")
         sys.exit(2)
 
