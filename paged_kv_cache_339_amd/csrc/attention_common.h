@@ -56,8 +56,10 @@ __device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
   const int pair = lin / p.num_kv_heads;          // < max_pairs by the grid size
   WorkItem it;
   it.h = lin - pair * p.num_kv_heads;
-  const int n_pairs = min(p.work->n_pairs, p.max_pairs);
+  // The pair is loaded before the list length so that both loads are in
+  // flight together (the other order made the compiler wait in between).
   const WorkPair wp = p.pairs[pair];
+  const int n_pairs = min(p.work->n_pairs, p.max_pairs);
   it.s = wp.s;
   it.part = wp.part;
   it.valid = pair < n_pairs && (unsigned)wp.s < (unsigned)p.num_seqs &&

@@ -49,6 +49,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   int tab = -1;
   if (lane < p.part_blocks && b0_guess + lane < p.max_blocks_per_seq) tab = table[b0_guess + lane];
 
+  // Query rows of the G heads that share this KV head: also fetched before
+  // the length arrives (widened and pre-scaled once it has), so the three
+  // loads overlap.
+  constexpr int QL = EPL * QES / 16;     // 16-byte query loads per head and lane
+  u32x4 qraw[G][QL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * QES;
+#pragma unroll
+    for (int l = 0; l < QL; ++l) qraw[g][l] = load16(qrow + 16 * l);
+  }
+
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
     if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
@@ -60,14 +73,11 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   }
   if (it.part >= sw.nparts) return;
 
-  // Query rows of the G heads that share this KV head, pre-scaled.
   float qf[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * QES;
 #pragma unroll
-    for (int l = 0; l < EPL * QES / 16; ++l) widen16<DT>(load16(qrow + 16 * l), qf[g] + l * (16 / QES));
+    for (int l = 0; l < QL; ++l) widen16<DT>(qraw[g][l], qf[g] + l * (16 / QES));
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[g][e] *= p.scale_log2;
   }
