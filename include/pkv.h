@@ -82,11 +82,19 @@ const char* pkv_last_error(void);
 /* Decode attention                                                          */
 /* ------------------------------------------------------------------------ */
 
+/* Both kernels take any number G of query heads per KV head (grouped-query
+ * attention: heads sharing one set of keys and values, "Paged Attention"
+ * glossary of systemdesign.academy; G = 1 is multi-head, Hkv = 1 multi-query).
+ * A workgroup computes up to 16 (MFMA) or 8 (VALU) of them; a larger group is
+ * cut into C = ceil(G / 16) (or ceil(G / 8)) equal chunks, one workgroup
+ * each, and the C workgroups of a (sequence, KV head, partition) run on one
+ * XCD so they read its key/value tiles through the same L2 (with plain
+ * loads, whatever the cache policy). */
 enum pkv_kernel {
-  PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit queries with 4..16 query heads per KV head, else VALU */
-  PKV_KERNEL_VALU = 1,  /* vector-ALU kernel: 1, 2, 4 or 8 query heads per KV head */
+  PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit queries with 3 or more query heads per KV head, else VALU */
+  PKV_KERNEL_VALU = 1,  /* vector-ALU kernel: every query / cache format */
   PKV_KERNEL_MFMA = 2   /* matrix-core kernel: f16/bf16 queries (8-bit caches decoded to that
-                           format), 4, 8 or 16 query heads per KV head */
+                           format); each chunk's heads padded to the 16 columns of the products */
 };
 
 /* How the attention kernels load keys and values (pkv_attn_options.cache_policy). */
@@ -197,14 +205,14 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * context_lens and writes the work list into the workspace (the
  * (sequence, partition) pairs, longest first, so long pieces start early
  * and the grid ends on short ones), then the main kernel, one workgroup per
- * (pair, KV head); and, when a sequence can span several partitions, the
+ * (pair, KV head, head chunk); and, when a sequence can span several partitions, the
  * split-K reduce, which merges the partial softmax states in partition
  * order.  The schedule does not change any result.
  * Data errors are contained, never dereferenced: a table entry outside
  * [0, num_blocks), or context_lens[s] above max_context_len or
  * max_blocks_per_seq * B, makes that sequence's output rows NaN.
- * head_dim: 64 or 128.  block_size: 8, 16, 32 or 64 (16 or 32 with 8-bit
- * caches).
+ * num_q_heads: any multiple of num_kv_heads.  head_dim: 64 or 128.
+ * block_size: 8, 16, 32 or 64 (16 or 32 with 8-bit caches).
  * workspace: device memory of at least pkv_paged_attention_workspace_bytes,
  * 16-byte aligned, required whenever num_seqs > 0; its contents need no
  * initialisation and are overwritten.  Calls that overlap in time must not

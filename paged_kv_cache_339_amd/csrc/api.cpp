@@ -54,7 +54,10 @@ bool pow2_block(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 struct Plan {
   int kernel;
   bool fp8;
-  bool keep;          // plain key/value loads (PKV_CACHE_KEEP)
+  bool keep;          // plain key/value loads (PKV_CACHE_KEEP, or head chunks)
+  int32_t chunks;     // workgroups per (sequence, KV head, partition)
+  int32_t chunk_rows; // query heads per chunk (the last may have fewer)
+  int32_t cap;        // instance's query heads per workgroup, >= chunk_rows
   int32_t window;
   int32_t part_blocks;
   int32_t max_parts;
@@ -86,17 +89,28 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
+  // Query heads per KV head: any G.  The matrix-core kernel pads a chunk of
+  // up to 16 heads to the 16 columns of its products, the vector kernel
+  // computes up to 8 per workgroup; a larger group is cut into C equal
+  // chunks, each a workgroup of its own that reads the same key/value tiles.
   const int group = num_q_heads / num_kv_heads;
   const bool sixteen_bit = dtype != PKV_F32;
-  const bool mfma_group = group == 4 || group == 8 || group == 16;
-  const bool valu_group = group == 1 || group == 2 || group == 4 || group == 8;
   int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
   if (kernel == PKV_KERNEL_AUTO)
-    kernel = (sixteen_bit && mfma_group) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
-  if (kernel == PKV_KERNEL_MFMA && !(sixteen_bit && mfma_group)) return PKV_ERR_UNSUPPORTED;
-  if (fp8 && (block_size == 8 || block_size == 64)) return PKV_ERR_UNSUPPORTED;
-  if (kernel == PKV_KERNEL_VALU && !valu_group) return PKV_ERR_UNSUPPORTED;
+    kernel = (sixteen_bit && group >= 3) ? PKV_KERNEL_MFMA : PKV_KERNEL_VALU;
   if (kernel != PKV_KERNEL_MFMA && kernel != PKV_KERNEL_VALU) return PKV_ERR_SHAPE;
+  if (kernel == PKV_KERNEL_MFMA && !sixteen_bit) return PKV_ERR_UNSUPPORTED;
+  if (fp8 && (block_size == 8 || block_size == 64)) return PKV_ERR_UNSUPPORTED;
+  const int max_rows = kernel == PKV_KERNEL_MFMA ? 16 : 8;
+  plan->chunks = (group + max_rows - 1) / max_rows;
+  plan->chunk_rows = (group + plan->chunks - 1) / plan->chunks;
+  if ((int64_t)(plan->chunks - 1) * plan->chunk_rows >= group) return PKV_ERR_SHAPE;
+  plan->cap = kernel == PKV_KERNEL_MFMA ? (plan->chunk_rows <= 4 ? 4 : plan->chunk_rows <= 8 ? 8 : 16)
+                                        : (plan->chunk_rows <= 2 ? plan->chunk_rows
+                                           : plan->chunk_rows <= 4 ? 4 : 8);
+  // Chunks of one item share its key/value tiles through L2, which the
+  // nontemporal loads would not fill.
+  if (plan->chunks > 1) plan->keep = true;
 
   // Partition boundaries must fall on block boundaries, and on 32-token
   // chunk boundaries for the MFMA kernel.
@@ -142,14 +156,17 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   }
   plan->window = window;
   plan->fp8 = fp8;
-  if ((int64_t)num_seqs * num_kv_heads * plan->max_parts > kMaxGrid) return PKV_ERR_SHAPE;
+  const int64_t items = (int64_t)num_seqs * num_kv_heads * plan->max_parts;
+  const int64_t grid = plan->chunks > 1 ? (items + 7) / 8 * 8 * plan->chunks : items;
+  if (grid > kMaxGrid) return PKV_ERR_SHAPE;
   plan->kernel = kernel;
   plan->max_pairs = (int64_t)num_seqs * plan->max_parts;
   plan->pairs_off = round_up(sizeof(pkv::WorkHeader), 256);
   plan->ws_o_off = plan->pairs_off + round_up((size_t)plan->max_pairs * sizeof(pkv::WorkPair), 256);
   plan->ws_ml_off = plan->ws_o_off;
   if (plan->max_parts > 1) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * plan->max_parts;
+    const size_t rows =
+        (size_t)num_seqs * num_kv_heads * plan->chunks * plan->max_parts * plan->cap;
     // Partition outputs are kept in the output format: the split-K writes
     // are the dearest bytes of a split (written into a saturated read stream).
     plan->ws_ml_off = plan->ws_o_off + round_up(rows * head_dim * dtype_bytes(dtype), 256);
@@ -284,9 +301,13 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.max_parts = plan.max_parts;
   p.max_pairs = (int32_t)plan.max_pairs;
   p.window = plan.window;
+  p.group = num_q_heads / num_kv_heads;
+  p.chunks = plan.chunks;
+  p.chunk_rows = plan.chunk_rows;
+  p.cap = plan.cap;
+  p.items = (int32_t)((int64_t)num_seqs * num_kv_heads * plan.max_parts);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int group = num_q_heads / num_kv_heads;
   clear_pending_error();
   const bool reuse = opts && opts->reuse_plan;
   hipError_t err = hipSuccess;
@@ -303,9 +324,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   }
   const bool have = plan.kernel == PKV_KERNEL_MFMA
                         ? pkv::launch_attention_mfma(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, group, plan.keep, s, &err)
+                                                     head_dim, block_size, plan.cap, plan.keep, s, &err)
                         : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, group, plan.keep, s, &err);
+                                                     head_dim, block_size, plan.cap, plan.keep, s, &err);
   if (!have) return PKV_ERR_UNSUPPORTED;
   if (err != hipSuccess) return launch_status(err);
   if (opts && opts->main_end_event) {

@@ -45,34 +45,54 @@ __device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
 // Safe reference point for 2^(x - m) when m may be -inf.
 __device__ __forceinline__ float softmax_ref(float m) { return m == -INFINITY ? 0.f : m; }
 
-// Workgroup -> (sequence, kv head, partition) through the plan: pair
-// blockIdx / Hkv of the list, KV head blockIdx % Hkv.  The grid covers every
-// pair the list could hold; workgroups past its end (and entries that do not
-// name a sequence and partition of this call) do nothing.
-struct WorkItem { int s, h, part; bool valid; };
+// Workgroup -> (sequence, KV head, head chunk, partition) through the plan.
+// Work item u covers pair u / Hkv of the list and KV head u % Hkv; the grid
+// covers every pair the list could hold, and workgroups past its end (and
+// entries that do not name a sequence and partition of this call) do
+// nothing.  With one chunk per KV head, workgroup u is item u.  With C > 1
+// chunks the C workgroups of one item are numbered 8 apart: workgroups are
+// dealt to the 8 XCDs in turn, so the chunks of an item run on one XCD at
+// about the same time and read the item's key/value tiles through the same
+// L2.
+struct WorkItem {
+  int s, h, part;  // sequence, KV head, partition
+  int slot;        // h * C + chunk: the item's run in the workspace
+  int q0, rows;    // first query head, query heads of the chunk
+  bool valid;
+};
 
 __device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
   const int lin = blockIdx.x;
-  const int pair = lin / p.num_kv_heads;          // < max_pairs by the grid size
+  int u = lin, c = 0;
+  if (p.chunks > 1) {
+    const int j = lin >> 3, jc = j / p.chunks;
+    u = jc * 8 + (lin & 7);
+    c = j - jc * p.chunks;
+  }
+  const bool in_grid = u < p.items;
+  const int pair = in_grid ? u / p.num_kv_heads : 0;
   WorkItem it;
-  it.h = lin - pair * p.num_kv_heads;
+  it.h = u - pair * p.num_kv_heads;
   // The pair is loaded before the list length so that both loads are in
   // flight together (the other order made the compiler wait in between).
   const WorkPair wp = p.pairs[pair];
   const int n_pairs = min(p.work->n_pairs, p.max_pairs);
   it.s = wp.s;
   it.part = wp.part;
-  it.valid = pair < n_pairs && (unsigned)wp.s < (unsigned)p.num_seqs &&
-             (unsigned)wp.part < (unsigned)p.max_parts;
+  it.slot = it.h * p.chunks + c;
+  it.q0 = it.h * p.group + c * p.chunk_rows;
+  it.rows = min(p.chunk_rows, p.group - c * p.chunk_rows);
+  it.valid = in_grid && pair < n_pairs && (unsigned)wp.s < (unsigned)p.num_seqs &&
+             (unsigned)wp.part < (unsigned)p.max_parts && it.rows > 0;
   return it;
 }
 
 // Rows that cannot be computed (data error) become NaN; empty sequences 0.
-template <int DT, int D, int G, int NT>
-__device__ __forceinline__ void fill_rows(const AttnParams& p, int s, int h, float value) {
-  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
+template <int DT, int D, int NT>
+__device__ __forceinline__ void fill_rows(const AttnParams& p, const WorkItem& it, float value) {
+  for (int idx = threadIdx.x; idx < it.rows * D; idx += NT) {
     const int g = idx / D, d = idx % D;
-    store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + h * G + g) * D + d, value);
+    store_elem<DT>(p.out, ((size_t)it.s * p.num_q_heads + it.q0 + g) * D + d, value);
   }
 }
 
@@ -85,22 +105,22 @@ struct MergeSmem {
   int bad[NW];
 };
 
-// After every wave has put its (m, l, o) for the G heads into `sm`: merge the
-// waves and store.  A sequence with one partition gets its final output row;
-// otherwise the partition's normalised output and (m, l) go to the
-// workspace for the reduce kernel, laid out [S, Hkv, P, G, D] (in the
-// output format) and [S, Hkv, P, G, 2] (fp32): one workgroup's G rows form
-// one contiguous run, and the partitions of a (sequence, KV head) follow each
-// other.  Written into the saturated read stream of the other workgroups,
-// these bytes cost far more than their share of the traffic, so they are
-// kept as narrow as the output itself.
+// After every wave has put its (m, l, o) for the chunk's heads into `sm`:
+// merge the waves and store.  A sequence with one partition gets its final
+// output rows; otherwise the partition's normalised output and (m, l) go to
+// the workspace for the reduce kernel, laid out [S, Hkv*C, P, cap, D] (in
+// the output format) and [S, Hkv*C, P, cap, 2] (fp32): one workgroup's rows
+// form one contiguous run, and the partitions of a (sequence, chunk) follow
+// each other.  Written into the saturated read stream of the other
+// workgroups, these bytes cost far more than their share of the traffic, so
+// they are kept as narrow as the output itself.
 template <int DT, int D, int G, int NW>
 __device__ __forceinline__ void merge_and_store(const AttnParams& p, const MergeSmem<D, G, NW>& sm,
-                                                int s, int h, int part, int nparts) {
+                                                const WorkItem& it, int nparts) {
   bool bad = false;
 #pragma unroll
   for (int w = 0; w < NW; ++w) bad |= sm.bad[w] != 0;
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+  for (int idx = threadIdx.x; idx < it.rows * D; idx += NW * kWave) {
     const int g = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -115,9 +135,10 @@ __device__ __forceinline__ void merge_and_store(const AttnParams& p, const Merge
     }
     const float r = bad ? __builtin_nanf("") : o / tot * p.v_scale;
     if (nparts == 1) {
-      store_elem<DT>(p.out, ((size_t)s * p.num_q_heads + h * G + g) * D + d, r);
+      store_elem<DT>(p.out, ((size_t)it.s * p.num_q_heads + it.q0 + g) * D + d, r);
     } else {
-      const size_t row0 = (((size_t)s * p.num_kv_heads + h) * p.max_parts + part) * G;
+      const size_t row0 =
+          (((size_t)it.s * p.num_kv_heads * p.chunks + it.slot) * p.max_parts + it.part) * G;
       store_elem<DT>(p.ws_o, row0 * D + idx, r);
       if (d == 0) {
         p.ws_ml[(row0 + g) * 2] = M;

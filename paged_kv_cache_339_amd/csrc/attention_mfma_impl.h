@@ -162,29 +162,29 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   const int b0_guess = it.part * p.part_blocks;
   int tab = b0_guess + lane < p.max_blocks_per_seq ? table[b0_guess + lane] : -1;
 
-  // Query rows of the G heads (the B operand of the score product), also
-  // fetched before the length.
+  // Query rows of the chunk's heads (the B operand of the score product),
+  // also fetched before the length; columns past the chunk are zero.
   const int r = lane & 15, q = lane >> 4;
   u32x4 qb[KS];
   {
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + (r < G ? r : 0)) * D + 8 * q) * ES;
+                       (((size_t)it.s * p.num_q_heads + it.q0 + (r < it.rows ? r : 0)) * D + 8 * q) * ES;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // Element offset of k-step ks past 8q: 32 ks, or for 8-bit caches
       // 64 (ks / 2) + 8 q + 8 (ks % 2) (the order the key loads give).
       const int off = F8 ? 64 * (ks / 2) + 8 * q + 8 * (ks % 2) : 32 * ks;
-      qb[ks] = (r < G) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
+      qb[ks] = (r < it.rows) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
     }
   }
 
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
+    if (it.part == 0) fill_rows<DT, D, NW * kWave>(p, it, __builtin_nanf(""));
     return;
   }
   if (sw.L == 0) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, 0.f);
+    if (it.part == 0) fill_rows<DT, D, NW * kWave>(p, it, 0.f);
     return;
   }
   if (it.part >= sw.nparts) return;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   l += shfl_xor_f(l, 32);
   const int any_bad = __any(bad);
 
-  if (r < G) {
+  if (r < it.rows) {
 #pragma unroll
     for (int n = 0; n < DPL; ++n)
 #pragma unroll
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   }
   if (lane == 0) sm.bad[w] = any_bad;
   __syncthreads();
-  merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
+  merge_and_store<DT, D, G, NW>(p, sm, it, sw.nparts);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +376,7 @@ constexpr int mfma_unroll() {
 
 template <int DT, int KT, int D, int B, int G, bool NT>
 hipError_t launch_mfma(const AttnParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
+  const dim3 grid((unsigned)attn_grid(p));
   hipLaunchKernelGGL((attn_mfma_kernel<DT, KT, D, B, G, kMfmaWaves, mfma_unroll<KT>(), NT>), grid,
                      dim3(kMfmaWaves * kWave), 0, st, p);
   return hipGetLastError();
@@ -424,16 +424,16 @@ bool mfma_by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipEr
 // separate translation units, so they compile in parallel).
 template <bool NT>
 bool mfma_dispatch(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim, int block_size,
-                   int group, hipStream_t stream, hipError_t* err) {
+                   int cap, hipStream_t stream, hipError_t* err) {
   const bool fp8 = kv == PKV_FP8_E4M3;
   if (!fp8 && kv != dt) return false;
   switch (dt) {
     case PKV_F16:
-      return fp8 ? mfma_by_dim<PKV_F16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, group, stream, err)
-                 : mfma_by_dim<PKV_F16, PKV_F16, NT>(p, head_dim, block_size, group, stream, err);
+      return fp8 ? mfma_by_dim<PKV_F16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, cap, stream, err)
+                 : mfma_by_dim<PKV_F16, PKV_F16, NT>(p, head_dim, block_size, cap, stream, err);
     case PKV_BF16:
-      return fp8 ? mfma_by_dim<PKV_BF16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, group, stream, err)
-                 : mfma_by_dim<PKV_BF16, PKV_BF16, NT>(p, head_dim, block_size, group, stream, err);
+      return fp8 ? mfma_by_dim<PKV_BF16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, cap, stream, err)
+                 : mfma_by_dim<PKV_BF16, PKV_BF16, NT>(p, head_dim, block_size, cap, stream, err);
     default: return false;
   }
 }

@@ -9,8 +9,9 @@
 
 namespace pkv {
 
-// One workgroup per (sequence, KV head): the G query heads' partials of a
-// partition are one contiguous run, read 4 elements per lane.  The merge runs over the partitions in order, as online softmax:
+// One workgroup per (sequence, head chunk): the chunk's rows of a partition
+// are one contiguous run, read 4 elements per lane.  The merge runs over the
+// partitions in order, as online softmax:
 // M' = max(M, m_p), W = W 2^(M - M') + l_p 2^(m_p - M'), and O likewise with
 // l_p 2^(m_p - M') o_p; the result O / W equals the two-pass form above.
 constexpr int kReduceThreads = 256;
@@ -30,14 +31,17 @@ constexpr int kReduceAhead = 4;     // partitions whose loads are in flight toge
 
 template <int DT, int D>
 __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams p, int B) {
-  const int Hkv = p.num_kv_heads;
-  const int G = p.num_q_heads / Hkv;
-  const int s = blockIdx.x / Hkv;
-  const int h = blockIdx.x - s * Hkv;
+  const int slots = p.num_kv_heads * p.chunks;
+  const int s = blockIdx.x / slots;
+  const int slot = blockIdx.x - s * slots;
+  const int c = slot % p.chunks;
+  const int q0 = slot / p.chunks * p.group + c * p.chunk_rows;
+  const int rows = min(p.chunk_rows, p.group - c * p.chunk_rows);
   const SeqWork sw = seq_work(p, s, B);
   if (sw.bad || sw.nparts <= 1) return;     // written by the main kernel
-  const size_t run0 = ((size_t)s * Hkv + h) * p.max_parts;   // partition 0's first row is run0 * G
-  for (int e = threadIdx.x * 4; e < G * D; e += blockDim.x * 4) {
+  const int G = p.cap;                      // rows per run in the workspace
+  const size_t run0 = ((size_t)s * slots + slot) * p.max_parts;   // partition 0's first row is run0 * G
+  for (int e = threadIdx.x * 4; e < rows * D; e += blockDim.x * 4) {
     const int g = e / D, d = e - g * D;
     float M = -INFINITY, W = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams 
         M = Mn;
       }
     }
-    const size_t out0 = ((size_t)s * p.num_q_heads + h * G + g) * D + d;
+    const size_t out0 = ((size_t)s * p.num_q_heads + q0 + g) * D + d;
     store_elem<DT>(p.out, out0, O.x / W);
     store_elem<DT>(p.out, out0 + 1, O.y / W);
     store_elem<DT>(p.out, out0 + 2, O.z / W);
@@ -78,9 +82,9 @@ __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams 
 namespace {
 template <int DT, int D>
 hipError_t launch_reduce(const AttnParams& p, int B, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads));
+  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.chunks));
   // Lanes take 4 elements each; small groups need fewer lanes.
-  const int rows = (p.num_q_heads / p.num_kv_heads) * D / 4;
+  const int rows = p.chunk_rows * D / 4;
   const int threads = min(kReduceThreads, max(kWave, (rows + kWave - 1) / kWave * kWave));
   hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(threads), 0, st, p, B);
   return hipGetLastError();

@@ -49,26 +49,27 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   int tab = -1;
   if (lane < p.part_blocks && b0_guess + lane < p.max_blocks_per_seq) tab = table[b0_guess + lane];
 
-  // Query rows of the G heads that share this KV head: also fetched before
-  // the length arrives (widened and pre-scaled once it has), so the three
-  // loads overlap.
+  // Query rows of the chunk's heads: also fetched before the length arrives
+  // (widened and pre-scaled once it has), so the three loads overlap.  Rows
+  // past the chunk repeat its last head; their results are never stored.
   constexpr int QL = EPL * QES / 16;     // 16-byte query loads per head and lane
   u32x4 qraw[G][QL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    const int qh = it.q0 + min(g, it.rows - 1);
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.h * G + g) * D + sub * EPL) * QES;
+                       (((size_t)it.s * p.num_q_heads + qh) * D + sub * EPL) * QES;
 #pragma unroll
     for (int l = 0; l < QL; ++l) qraw[g][l] = load16(qrow + 16 * l);
   }
 
   const SeqWork sw = seq_work(p, it.s, B);
   if (sw.bad) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, __builtin_nanf(""));
+    if (it.part == 0) fill_rows<DT, D, NW * kWave>(p, it, __builtin_nanf(""));
     return;
   }
   if (sw.L == 0) {
-    if (it.part == 0) fill_rows<DT, D, G, NW * kWave>(p, it.s, it.h, 0.f);
+    if (it.part == 0) fill_rows<DT, D, NW * kWave>(p, it, 0.f);
     return;
   }
   if (it.part >= sw.nparts) return;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
     sm.bad[w] = __any(bad);
   }
   __syncthreads();
-  merge_and_store<DT, D, G, NW>(p, sm, it.s, it.h, it.part, sw.nparts);
+  merge_and_store<DT, D, G, NW>(p, sm, it, sw.nparts);
 }
 
 // ---------------------------------------------------------------------------
@@ -247,7 +248,7 @@ constexpr int valu_unroll() {
 
 template <int DT, int KT, int D, int B, int G, bool NT>
 hipError_t launch_valu(const AttnParams& p, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.max_parts));
+  const dim3 grid((unsigned)attn_grid(p));
   hipLaunchKernelGGL((attn_valu_kernel<DT, KT, D, B, G, kValuWaves, valu_unroll<DT, KT, D, G>(), NT>),
                      grid, dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
   return hipGetLastError();
@@ -292,19 +293,19 @@ bool valu_by_dim(const AttnParams& p, int D, int B, int G, hipStream_t st, hipEr
 // separate translation units, so they compile in parallel).
 template <bool NT>
 bool valu_dispatch(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim, int block_size,
-                   int group, hipStream_t stream, hipError_t* err) {
+                   int cap, hipStream_t stream, hipError_t* err) {
   if (kv == PKV_FP8_E4M3) {
     switch (dt) {
-      case PKV_F16: return valu_by_dim<PKV_F16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, group, stream, err);
-      case PKV_BF16: return valu_by_dim<PKV_BF16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, group, stream, err);
+      case PKV_F16: return valu_by_dim<PKV_F16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, cap, stream, err);
+      case PKV_BF16: return valu_by_dim<PKV_BF16, PKV_FP8_E4M3, NT>(p, head_dim, block_size, cap, stream, err);
       default: return false;
     }
   }
   if (kv != dt) return false;
   switch (dt) {
-    case PKV_F32: return valu_by_dim<PKV_F32, PKV_F32, NT>(p, head_dim, block_size, group, stream, err);
-    case PKV_F16: return valu_by_dim<PKV_F16, PKV_F16, NT>(p, head_dim, block_size, group, stream, err);
-    case PKV_BF16: return valu_by_dim<PKV_BF16, PKV_BF16, NT>(p, head_dim, block_size, group, stream, err);
+    case PKV_F32: return valu_by_dim<PKV_F32, PKV_F32, NT>(p, head_dim, block_size, cap, stream, err);
+    case PKV_F16: return valu_by_dim<PKV_F16, PKV_F16, NT>(p, head_dim, block_size, cap, stream, err);
+    case PKV_BF16: return valu_by_dim<PKV_BF16, PKV_BF16, NT>(p, head_dim, block_size, cap, stream, err);
     default: return false;
   }
 }

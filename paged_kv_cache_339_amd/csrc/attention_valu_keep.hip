@@ -6,8 +6,8 @@
 namespace pkv {
 
 bool launch_attention_valu_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                                int block_size, int group, hipStream_t stream, hipError_t* err) {
-  return valu_dispatch<false>(p, dt, kv, head_dim, block_size, group, stream, err);
+                                int block_size, int cap, hipStream_t stream, hipError_t* err) {
+  return valu_dispatch<false>(p, dt, kv, head_dim, block_size, cap, stream, err);
 }
 
 }  // namespace pkv

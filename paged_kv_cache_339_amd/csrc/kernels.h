@@ -29,8 +29,8 @@ struct AttnParams {
   const void* v_cache;
   const int32_t* block_tables;  // [S, M]
   const int32_t* context_lens;  // [S]
-  void* ws_o;                 // [S, Hkv, P, G, D] partition outputs, normalised, output format
-  float* ws_ml;               // [S, Hkv, P, G, 2] (running max in log2 units, sum)
+  void* ws_o;                 // [S, Hkv*C, P, cap, D] partition outputs, normalised, output format
+  float* ws_ml;               // [S, Hkv*C, P, cap, 2] (running max in log2 units, sum)
   WorkHeader* work;           // plan written by the plan kernel
   WorkPair* pairs;            // [max_pairs]
   float scale_log2;           // scale * log2(e), times k_scale for 8-bit caches
@@ -45,25 +45,42 @@ struct AttnParams {
   int32_t max_parts;          // partitions per sequence covered by the grid
   int32_t max_pairs;          // num_seqs * max_parts, the room of `pairs`
   int32_t window;             // sliding window in tokens, 0 = attend to all
+  // Query heads: the G = Hq / Hkv heads of one KV head are served in C
+  // chunks of at most R = ceil(G / C) heads, one workgroup per chunk; a
+  // workgroup holds room for `cap` heads (its kernel's compile-time group).
+  int32_t group;              // G
+  int32_t chunks;             // C
+  int32_t chunk_rows;         // R
+  int32_t cap;                // rows per (sequence, chunk, partition) in the workspace
+  int32_t items;              // S * Hkv * max_parts, work items per chunk
 };
 
-// Returns false when no kernel instance exists for the combination.
+// Workgroups of a main-kernel launch: one per work item and head chunk;
+// with several chunks the grid is rounded up to whole rounds of the 8 XCDs
+// (the numbering work_item undoes).
+inline size_t attn_grid(const AttnParams& p) {
+  if (p.chunks <= 1) return (size_t)p.items;
+  return ((size_t)p.items + 7) / 8 * 8 * (size_t)p.chunks;
+}
+
+// Returns false when no kernel instance exists for the combination; `cap`
+// selects the instance (rows per workgroup, AttnParams::cap).
 // dt: the query / output format; kv: the caches' (dt, or PKV_FP8_E4M3);
 // keep: plain key/value loads (blocks shared across the batch are served
 // again from cache) instead of nontemporal ones.
 bool launch_attention_valu(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                           int block_size, int group, bool keep, hipStream_t stream, hipError_t* err);
+                           int block_size, int cap, bool keep, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                           int block_size, int group, bool keep, hipStream_t stream, hipError_t* err);
+                           int block_size, int cap, bool keep, hipStream_t stream, hipError_t* err);
 // The two load policies' instances, each built in a translation unit of its own.
 bool launch_attention_valu_stream(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                                  int block_size, int group, hipStream_t stream, hipError_t* err);
+                                  int block_size, int cap, hipStream_t stream, hipError_t* err);
 bool launch_attention_valu_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                                int block_size, int group, hipStream_t stream, hipError_t* err);
+                                int block_size, int cap, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma_stream(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                                  int block_size, int group, hipStream_t stream, hipError_t* err);
+                                  int block_size, int cap, hipStream_t stream, hipError_t* err);
 bool launch_attention_mfma_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv, int head_dim,
-                                int block_size, int group, hipStream_t stream, hipError_t* err);
+                                int block_size, int cap, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
 
 // New tokens of a decode step (one per sequence), stored by the launch that

@@ -53,7 +53,7 @@ def decode(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(out=None), -1), (dict(q=None), -1), (dict(tables=None), -1), (dict(lens=None), -1),
     (dict(dtype=7), -3), (dict(D=96), -4), (dict(D=256), -4), (dict(B=12), -4), (dict(B=128), -4),
-    (dict(Hq=3), -2), (dict(Hq=6, Hkv=2), -4), (dict(S=-1), -2), (dict(max_ctx=-5), -2),
+    (dict(Hq=3), -2), (dict(Hq=6, Hkv=4), -2), (dict(S=-1), -2), (dict(max_ctx=-5), -2),
     (dict(M=0), -2), (dict(N=0), -2), (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
     (dict(q=ctypes.c_void_p(0x1008)), -5), (dict(k=ctypes.c_void_p(0x1004)), -5),
     (dict(max_ctx=5000), -6),                             # needs a split-K workspace
@@ -71,6 +71,16 @@ def test_decode_mfma_only_for_16_bit_groups():
     assert decode(opts=ctypes.byref(bad_part), max_ctx=5000) == -2     # not a multiple of B
     bad_mfma_part = AttnOptions(16, 2, None, None)
     assert decode(opts=ctypes.byref(bad_mfma_part), dtype=2, Hq=16, Hkv=2, max_ctx=5000) == -2
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,kernel", [(0, 6, 2, 0), (0, 48, 2, 1), (2, 10, 2, 0), (2, 71, 1, 0),
+                                                 (1, 2, 2, 2), (1, 4, 2, 2), (2, 48, 1, 1)])
+def test_decode_accepts_any_group(dtype, Hq, Hkv, kernel):
+    """Every multiple of the KV heads is a valid group on both kernels (the
+    matrix cores take 16-bit queries only): such calls get as far as the
+    workspace check, which comes before any launch."""
+    opts = AttnOptions(0, kernel, None, None)
+    assert decode(opts=ctypes.byref(opts), dtype=dtype, Hq=Hq, Hkv=Hkv, max_ctx=5000) == -6
 
 
 def test_empty_batch_is_a_no_op():
@@ -171,6 +181,13 @@ def test_plan_info_reports_the_launch():
     assert info(256, 16, 2, 128, 32, 32768, 2) == (4096, 8, "mfma")             # GQA layer, TP-4 share
     assert info(16, 32, 8, 128, 16, 16384, 2, sliding_window=4096) == (832, 5, "mfma")   # 257 blocks / 5
     assert info(64, 32, 32, 128, 16, 2048, 1, partition_size=48) == (48, 43, "valu")
+    # Any group: 16-bit queries from 3 heads per KV head on the matrix cores.
+    assert info(256, 40, 8, 128, 16, 4096, 2) == (4096, 1, "mfma")              # G = 5
+    assert info(64, 28, 4, 128, 16, 4096, 1)[2] == "mfma"                       # G = 7
+    assert info(64, 6, 2, 128, 16, 4096, 1)[2] == "mfma"                        # G = 3
+    assert info(64, 4, 2, 128, 16, 4096, 1)[2] == "valu"                        # G = 2
+    assert info(64, 71, 1, 64, 16, 4096, 2)[2] == "mfma"                        # multi-query, G = 71
+    assert info(64, 12, 4, 128, 16, 4096, 0)[2] == "valu"                       # fp32, G = 3
     with pytest.raises(pkv.PkvError):
         info(4, 2, 2, 96, 16, 64, 0)                                             # head_dim 96
     with pytest.raises(pkv.PkvError):
@@ -182,6 +199,34 @@ def test_plan_info_reports_the_launch():
             rows = args[0] * args[1] * parts
             want += _up(rows * args[3] * (4 if args[6] == 0 else 2)) + _up(rows * 2 * 4)
         assert pkv.workspace_bytes(*args) == want
+
+
+def test_workspace_rows_follow_the_head_chunks():
+    """With split-K, each (sequence, KV head, chunk, partition) has room for
+    the instance's rows: chunks of at most 16 (matrix cores, padded to 4, 8
+    or 16) or 8 (vector kernel) query heads, the group cut into equal
+    chunks."""
+    def ws_rows(S, Hq, Hkv, dtype, kernel, chunks, cap, parts):
+        n = pkv.workspace_bytes(S, Hq, Hkv, 64, 16, 4096, dtype, partition_size=512, kernel=kernel)
+        rows = S * Hkv * chunks * parts * cap
+        es = 4 if dtype == 0 else 2
+        return n == 256 + _up(S * parts * 8) + _up(rows * 64 * es) + _up(rows * 2 * 4)
+    assert ws_rows(3, 71, 1, 2, "auto", 5, 16, 8)        # 71 = 4 x 15 + 11
+    assert ws_rows(3, 10, 2, 2, "auto", 1, 8, 8)         # 5 -> 8 columns
+    assert ws_rows(3, 6, 2, 2, "auto", 1, 4, 8)          # 3 -> 4 columns
+    assert ws_rows(3, 24, 1, 1, "valu", 3, 8, 8)         # 24 = 3 x 8
+    assert ws_rows(3, 12, 1, 0, "valu", 2, 8, 8)         # 12 = 2 x 6, 8 rows of room
+    assert ws_rows(3, 6, 2, 0, "valu", 1, 4, 8)          # 3 -> 4 rows of room
+
+
+def test_chunked_grids_count_against_the_dispatch_limit():
+    """Head chunks multiply the workgroups of a launch (rounded to whole
+    rounds of 8): the limit applies to that count."""
+    # 65536 x 1 x 2 chunks x 128 partitions = 2^24 workgroups > 2^32 / 256.
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_info(65536, 32, 1, 64, 16, 8192, 1, partition_size=64)
+    assert e.value.status == -2
+    assert pkv.plan_info(65536, 16, 1, 64, 16, 8192, 1, partition_size=64)[1] == 128   # one chunk: fits
 
 
 def test_launches_beyond_the_dispatch_limit_are_refused():
