@@ -55,6 +55,7 @@ LENGTH_DESC = {
     6: "uniform [1024, 16384], attention over the last 4096",
     8: "uniform [128, 2048]",
     9: "uniform [1024, 32768]",
+    10: "uniform [1024, 8192]",
 }
 
 

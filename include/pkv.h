@@ -85,11 +85,13 @@ const char* pkv_last_error(void);
 /* Both kernels take any number G of query heads per KV head (grouped-query
  * attention: heads sharing one set of keys and values, "Paged Attention"
  * glossary of systemdesign.academy; G = 1 is multi-head, Hkv = 1 multi-query).
- * A workgroup computes up to 16 (MFMA) or 8 (VALU) of them; a larger group is
- * cut into C = ceil(G / 16) (or ceil(G / 8)) equal chunks, one workgroup
- * each, and the C workgroups of a (sequence, KV head, partition) run on one
- * XCD so they read its key/value tiles through the same L2 (with plain
- * loads, whatever the cache policy). */
+ * A workgroup computes up to 8 of them on the vector ALUs; on the matrix
+ * cores up to 16, or with 16- and 32-token blocks up to 64 (head_dim 64) or
+ * 32 (head_dim 128) as several 16-column tiles that share each key/value
+ * load.  A larger group is cut into C equal chunks, one workgroup each, and
+ * the C workgroups of a (sequence, KV head, partition) run on one XCD so
+ * they read its key/value tiles through the same L2 (with plain loads,
+ * whatever the cache policy). */
 enum pkv_kernel {
   PKV_KERNEL_AUTO = 0,  /* MFMA for 16-bit queries with 3 or more query heads per KV head, else VALU */
   PKV_KERNEL_VALU = 1,  /* vector-ALU kernel: every query / cache format */

@@ -89,10 +89,11 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (!pow2_block(block_size)) return PKV_ERR_UNSUPPORTED;
-  // Query heads per KV head: any G.  The matrix-core kernel pads a chunk of
-  // up to 16 heads to the 16 columns of its products, the vector kernel
-  // computes up to 8 per workgroup; a larger group is cut into C equal
-  // chunks, each a workgroup of its own that reads the same key/value tiles.
+  // Query heads per KV head: any G.  The matrix-core kernel pads a chunk's
+  // heads to whole 16-column tiles of its products (up to 64 heads), the
+  // vector kernel computes up to 8 per workgroup; a larger group is cut into
+  // C equal chunks, each a workgroup of its own that reads the same
+  // key/value tiles.
   const int group = num_q_heads / num_kv_heads;
   const bool sixteen_bit = dtype != PKV_F32;
   int kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
@@ -101,13 +102,19 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   if (kernel != PKV_KERNEL_MFMA && kernel != PKV_KERNEL_VALU) return PKV_ERR_SHAPE;
   if (kernel == PKV_KERNEL_MFMA && !sixteen_bit) return PKV_ERR_UNSUPPORTED;
   if (fp8 && (block_size == 8 || block_size == 64)) return PKV_ERR_UNSUPPORTED;
-  const int max_rows = kernel == PKV_KERNEL_MFMA ? 16 : 8;
+  // Matrix cores: up to 4 (head_dim 64) or 2 (128) column tiles of 16
+  // heads per wave with 16- and 32-token blocks, one tile otherwise.
+  const int tiles = kernel != PKV_KERNEL_MFMA ? 1
+                    : (block_size == 16 || block_size == 32) ? (head_dim == 64 ? 4 : 2) : 1;
+  const int max_rows = kernel == PKV_KERNEL_MFMA ? 16 * tiles : 8;
   plan->chunks = (group + max_rows - 1) / max_rows;
   plan->chunk_rows = (group + plan->chunks - 1) / plan->chunks;
   if ((int64_t)(plan->chunks - 1) * plan->chunk_rows >= group) return PKV_ERR_SHAPE;
-  plan->cap = kernel == PKV_KERNEL_MFMA ? (plan->chunk_rows <= 4 ? 4 : plan->chunk_rows <= 8 ? 8 : 16)
-                                        : (plan->chunk_rows <= 2 ? plan->chunk_rows
-                                           : plan->chunk_rows <= 4 ? 4 : 8);
+  const int rows = plan->chunk_rows;
+  if (kernel == PKV_KERNEL_MFMA)
+    plan->cap = rows <= 4 ? 4 : rows <= 8 ? 8 : (rows + 15) / 16 * 16;
+  else
+    plan->cap = rows <= 2 ? rows : rows <= 4 ? 4 : 8;
   // Chunks of one item share its key/value tiles through L2, which the
   // nontemporal loads would not fill.
   if (plan->chunks > 1) plan->keep = true;

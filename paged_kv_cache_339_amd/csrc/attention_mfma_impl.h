@@ -6,10 +6,13 @@
 // dense contractions:
 //     scores^T [32 tok x 16]  = K [32 tok x D] * Q^T [D x 16]
 //     out^T    [D x 16]      += V^T [D x 32 tok] * P^T [32 tok x 16]
-// with the G heads padded to the 16 columns of v_mfma_f32_16x16x32_{bf16,f16}
+// with the heads padded to the 16 columns of v_mfma_f32_16x16x32_{bf16,f16}
 // (fp32 accumulate).  Keys and values are still read once, through the
 // block table, exactly as in the vector-ALU kernel; the workgroup layout
-// (sequence, KV head, split-K partition) and the epilogue are shared.
+// (sequence, KV head, head chunk, split-K partition) and the epilogue are
+// shared.  A workgroup of more than 16 heads (multi-query layers) keeps one
+// set of accumulators per 16-column tile: every key and value register a
+// wave loads feeds all of its tiles, so the heads do not re-read the cache.
 //
 // Operand layouts of the 16x16x32 MFMA (lane l, r = l % 16, q = l / 16):
 //   A (16 x 32): lane holds A[r][8q .. 8q+7]
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   constexpr int KL = F8 ? KS / 2 : KS;   // 16-byte key loads per token row and lane
   constexpr int DPL = D / 16;     // value elements per lane per token
   constexpr int CH = 32;          // tokens per chunk
-  static_assert(G >= 1 && G <= 16, "query group must fit 16 MFMA columns");
+  constexpr int T = (G + 15) / 16;  // 16-head column tiles per wave
+  static_assert(G >= 1 && (G <= 16 || G % 16 == 0), "query heads: up to 16, or whole tiles of 16");
   static_assert(B >= 8, "8 consecutive tokens of a lane must share a block");
   using Ops = Mfma<DT>;
   using VL = VLoad<DT, KT, DPL>;
@@ -163,18 +167,21 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   int tab = b0_guess + lane < p.max_blocks_per_seq ? table[b0_guess + lane] : -1;
 
   // Query rows of the chunk's heads (the B operand of the score product),
-  // also fetched before the length; columns past the chunk are zero.
+  // also fetched before the length: head 16 ct + r of the chunk in column
+  // tile ct; columns past the chunk are zero.
   const int r = lane & 15, q = lane >> 4;
-  u32x4 qb[KS];
-  {
+  u32x4 qb[T][KS];
+#pragma unroll
+  for (int ct = 0; ct < T; ++ct) {
+    const int hr = 16 * ct + r;
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (((size_t)it.s * p.num_q_heads + it.q0 + (r < it.rows ? r : 0)) * D + 8 * q) * ES;
+                       (((size_t)it.s * p.num_q_heads + it.q0 + (hr < it.rows ? hr : 0)) * D + 8 * q) * ES;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // Element offset of k-step ks past 8q: 32 ks, or for 8-bit caches
       // 64 (ks / 2) + 8 q + 8 (ks % 2) (the order the key loads give).
       const int off = F8 ? 64 * (ks / 2) + 8 * q + 8 * (ks % 2) : 32 * ks;
-      qb[ks] = (r < it.rows) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
+      qb[ct][ks] = (hr < it.rows) ? load16(qrow + off * ES) : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -191,10 +198,15 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 
   const int Hkv = p.num_kv_heads, L = sw.L, t0 = sw.t0, N = p.num_blocks;
 
-  f32x4 o[DPL];
+  f32x4 o[T][DPL];
+  float m[T], l[T];
 #pragma unroll
-  for (int n = 0; n < DPL; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int ct = 0; ct < T; ++ct) {
+#pragma unroll
+    for (int n = 0; n < DPL; ++n) o[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[ct] = -INFINITY;
+    l[ct] = 0.f;
+  }
   int bad = 0;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_cache);
@@ -266,53 +278,60 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
     for (int u = 0; u < U; ++u) {
       const int c0 = c00 + u * CH;
       if (c0 >= te) break;
-      // Scores of head r for tokens c0 + 8q + j, j = 4t + i.
-      float sc[8];
+      // Every column tile uses the chunk's key and value registers: scores
+      // of head 16 ct + r for tokens c0 + 8q + j, j = 4t + i, the online
+      // softmax step, then the weights in the operand format.
+      u32x4 pb[T];
+      float alpha[T];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < T; ++ct) {
+        float sc[8];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 a;
-          if constexpr (F8) {
-            const u32x4 w = kr[u][t][ks / 2];
-            a = (ks % 2) ? decode8_e4m3<DT>(w[2], w[3]) : decode8_e4m3<DT>(w[0], w[1]);
-          } else {
-            a = kr[u][t][ks];
+        for (int t = 0; t < 2; ++t) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            u32x4 a;
+            if constexpr (F8) {
+              const u32x4 w = kr[u][t][ks / 2];
+              a = (ks % 2) ? decode8_e4m3<DT>(w[2], w[3]) : decode8_e4m3<DT>(w[0], w[1]);
+            } else {
+              a = kr[u][t][ks];
+            }
+            acc = Ops::mma(a, qb[ct][ks], acc);
           }
-          acc = Ops::mma(a, qb[ks], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i] * p.scale_log2;
         }
+        if (c0 + CH > L || c0 < t0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[4 * t + i] = acc[i] * p.scale_log2;
-      }
-      if (c0 + CH > L || c0 < t0) {
+          for (int j = 0; j < 8; ++j)
+            if (c0 + 8 * q + j >= L || c0 + 8 * q + j < t0) sc[j] = -INFINITY;
+        }
+
+        float cm = sc[0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c0 + 8 * q + j >= L || c0 + 8 * q + j < t0) sc[j] = -INFINITY;
+        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
+        cm = fmaxf(cm, shfl_xor_f(cm, 16));
+        cm = fmaxf(cm, shfl_xor_f(cm, 32));
+        const float mn = fmaxf(m[ct], cm);
+        const float ref = softmax_ref(mn);
+        alpha[ct] = fast_exp2(m[ct] - ref);
+        m[ct] = mn;
+
+        // Weights rounded to the operand format; the sum uses the rounded values.
+        float ps = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = Ops::narrow(fast_exp2(sc[2 * k] - ref));
+          const uint32_t hi = Ops::narrow(fast_exp2(sc[2 * k + 1] - ref));
+          pb[ct][k] = lo | (hi << 16);
+          ps += widen_half<DT>(pb[ct][k], false) + widen_half<DT>(pb[ct][k], true);
+        }
+        l[ct] = fmaf(l[ct], alpha[ct], ps);
       }
 
-      float cm = sc[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
-      cm = fmaxf(cm, shfl_xor_f(cm, 16));
-      cm = fmaxf(cm, shfl_xor_f(cm, 32));
-      const float mn = fmaxf(m, cm);
-      const float ref = softmax_ref(mn);
-      const float alpha = fast_exp2(m - ref);
-      m = mn;
-
-      // Weights rounded to the operand format; the sum uses the rounded values.
-      u32x4 pb;
-      float ps = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = Ops::narrow(fast_exp2(sc[2 * k] - ref));
-        const uint32_t hi = Ops::narrow(fast_exp2(sc[2 * k + 1] - ref));
-        pb[k] = lo | (hi << 16);
-        ps += widen_half<DT>(pb[k], false) + widen_half<DT>(pb[k], true);
-      }
-      l = fmaf(l, alpha, ps);
-
+      // Value product: each transposed operand row serves every tile.
       typename VRow<DPL>::type v16[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v16[j] = VL::widen(vr[u][j]);
@@ -323,24 +342,34 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           a[k] = __builtin_amdgcn_perm(v16[2 * k + 1][n >> 1], v16[2 * k][n >> 1], sel);
-        o[n] *= alpha;
-        o[n] = Ops::mma(a, pb, o[n]);
+#pragma unroll
+        for (int ct = 0; ct < T; ++ct) {
+          o[ct][n] *= alpha[ct];
+          o[ct][n] = Ops::mma(a, pb[ct], o[ct][n]);
+        }
       }
     }
   }
 
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
+#pragma unroll
+  for (int ct = 0; ct < T; ++ct) {
+    l[ct] += shfl_xor_f(l[ct], 16);
+    l[ct] += shfl_xor_f(l[ct], 32);
+  }
   const int any_bad = __any(bad);
 
-  if (r < it.rows) {
 #pragma unroll
-    for (int n = 0; n < DPL; ++n)
+  for (int ct = 0; ct < T; ++ct) {
+    const int hr = 16 * ct + r;
+    if (hr < it.rows) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.o[w][r][DPL * (4 * q + i) + n] = o[n][i];
-    if (q == 0) {
-      sm.m[w][r] = m;
-      sm.l[w][r] = l;
+      for (int n = 0; n < DPL; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.o[w][hr][DPL * (4 * q + i) + n] = o[ct][n][i];
+      if (q == 0) {
+        sm.m[w][hr] = m[ct];
+        sm.l[w][hr] = l[ct];
+      }
     }
   }
   if (lane == 0) sm.bad[w] = any_bad;
@@ -382,12 +411,25 @@ hipError_t launch_mfma(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Query heads per workgroup: 4, 8 or 16 in one column tile; with 16- and
+// 32-token blocks also 2 (head_dim 128) or up to 4 (head_dim 64) tiles, as
+// many as the registers hold next to the accumulators.
 template <int DT, int KT, int D, int B, bool NT>
 bool mfma_by_group(const AttnParams& p, int G, hipStream_t st, hipError_t* e) {
+  constexpr bool kTiles = B == 16 || B == 32;
   switch (G) {
     case 4: *e = launch_mfma<DT, KT, D, B, 4, NT>(p, st); return true;
     case 8: *e = launch_mfma<DT, KT, D, B, 8, NT>(p, st); return true;
     case 16: *e = launch_mfma<DT, KT, D, B, 16, NT>(p, st); return true;
+    case 32:
+      if constexpr (kTiles) { *e = launch_mfma<DT, KT, D, B, 32, NT>(p, st); return true; }
+      return false;
+    case 48:
+      if constexpr (kTiles && D == 64) { *e = launch_mfma<DT, KT, D, B, 48, NT>(p, st); return true; }
+      return false;
+    case 64:
+      if constexpr (kTiles && D == 64) { *e = launch_mfma<DT, KT, D, B, 64, NT>(p, st); return true; }
+      return false;
     default: return false;
   }
 }

@@ -102,6 +102,13 @@ CONFIGS = {
     9: DecodeConfig("gqa70b_layer_fp8kv", num_seqs=256, num_q_heads=64, num_kv_heads=8,
                     head_dim=128, dtype="bf16", block_size=32, lengths="uniform",
                     len_lo=1024, len_hi=32768, kv_format="fp8_e4m3", k_scale=1.0 / 32, v_scale=1.0 / 32),
+    # A multi-query layer (Falcon-7B-like: 71 query heads over one KV head,
+    # head_dim 64): the group is larger than one workgroup computes, so each
+    # (sequence, partition) is served by 5 workgroups of 15, 15, 15, 15 and
+    # 11 heads that read the same key/value tiles.
+    10: DecodeConfig("mqa_falcon7b_layer_bf16", num_seqs=256, num_q_heads=71, num_kv_heads=1,
+                     head_dim=64, dtype="bf16", block_size=16, lengths="uniform",
+                     len_lo=1024, len_hi=8192),
 }
 
 

@@ -203,15 +203,21 @@ def test_plan_info_reports_the_launch():
 
 def test_workspace_rows_follow_the_head_chunks():
     """With split-K, each (sequence, KV head, chunk, partition) has room for
-    the instance's rows: chunks of at most 16 (matrix cores, padded to 4, 8
-    or 16) or 8 (vector kernel) query heads, the group cut into equal
-    chunks."""
-    def ws_rows(S, Hq, Hkv, dtype, kernel, chunks, cap, parts):
-        n = pkv.workspace_bytes(S, Hq, Hkv, 64, 16, 4096, dtype, partition_size=512, kernel=kernel)
+    the instance's rows: chunks of at most 64 (matrix cores at head_dim 64
+    with 16- or 32-token blocks; 32 at head_dim 128, 16 with other blocks),
+    padded to 4, 8 or whole 16-column tiles, or 8 (vector kernel) query
+    heads, the group cut into equal chunks."""
+    def ws_rows(S, Hq, Hkv, dtype, kernel, chunks, cap, parts, D=64, B=16):
+        n = pkv.workspace_bytes(S, Hq, Hkv, D, B, 4096, dtype, partition_size=512, kernel=kernel)
         rows = S * Hkv * chunks * parts * cap
         es = 4 if dtype == 0 else 2
-        return n == 256 + _up(S * parts * 8) + _up(rows * 64 * es) + _up(rows * 2 * 4)
-    assert ws_rows(3, 71, 1, 2, "auto", 5, 16, 8)        # 71 = 4 x 15 + 11
+        return n == 256 + _up(S * parts * 8) + _up(rows * D * es) + _up(rows * 2 * 4)
+    assert ws_rows(3, 71, 1, 2, "auto", 2, 48, 8)        # 71 = 36 + 35 in 3 tiles
+    assert ws_rows(3, 64, 1, 2, "auto", 1, 64, 8)        # 4 tiles
+    assert ws_rows(3, 128, 1, 1, "auto", 2, 64, 8)       # 2 x 64
+    assert ws_rows(3, 71, 1, 2, "auto", 5, 16, 8, B=8)   # 8-token blocks: one tile, 4 x 15 + 11
+    assert ws_rows(3, 40, 1, 2, "auto", 2, 32, 8, D=128, B=32)   # head_dim 128: 2 x 20 in 2 tiles
+    assert ws_rows(3, 32, 1, 2, "auto", 1, 32, 8, D=128)
     assert ws_rows(3, 10, 2, 2, "auto", 1, 8, 8)         # 5 -> 8 columns
     assert ws_rows(3, 6, 2, 2, "auto", 1, 4, 8)          # 3 -> 4 columns
     assert ws_rows(3, 24, 1, 1, "valu", 3, 8, 8)         # 24 = 3 x 8
@@ -224,9 +230,9 @@ def test_chunked_grids_count_against_the_dispatch_limit():
     rounds of 8): the limit applies to that count."""
     # 65536 x 1 x 2 chunks x 128 partitions = 2^24 workgroups > 2^32 / 256.
     with pytest.raises(pkv.PkvError) as e:
-        pkv.plan_info(65536, 32, 1, 64, 16, 8192, 1, partition_size=64)
+        pkv.plan_info(65536, 72, 1, 64, 16, 8192, 1, partition_size=64)
     assert e.value.status == -2
-    assert pkv.plan_info(65536, 16, 1, 64, 16, 8192, 1, partition_size=64)[1] == 128   # one chunk: fits
+    assert pkv.plan_info(65536, 64, 1, 64, 16, 8192, 1, partition_size=64)[1] == 128   # one chunk: fits
 
 
 def test_launches_beyond_the_dispatch_limit_are_refused():

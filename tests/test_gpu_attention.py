@@ -39,6 +39,7 @@ def test_config1_every_row(partition_size):
 
 
 SCALED = {
+    10: dict(num_seqs=5),
     9: dict(num_seqs=3),
     8: dict(num_seqs=6),
     6: dict(num_seqs=6),
@@ -49,7 +50,7 @@ SCALED = {
 }
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8, 9])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8, 9, 10])
 def test_scaled_workloads_every_row(idx):
     cfg = CONFIGS[idx].scaled(**SCALED[idx])
     run_case(cfg, seed=10 + idx, partition_size=cfg.partition_size, label=f"config{idx}-scaled")
@@ -220,7 +221,7 @@ def test_work_list_covers_every_partition_longest_first():
     assert rest[-2:] == [0, 0], "empty sequences come last"
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 8, 9])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 8, 9, 10])
 def test_decode_step_equals_scatter_then_attend(idx):
     """The fused step stores the same bytes and returns the same bits as
     reshape_and_cache followed by paged_attention_decode, and matches the
@@ -310,7 +311,7 @@ def _sign_flipped(t: torch.Tensor) -> torch.Tensor:
     return (t.view(view) ^ bits).view(t.dtype)
 
 
-@pytest.mark.parametrize("idx,partition_size", [(3, 0), (4, 0), (4, 256), (6, 0), (8, 0), (9, 0), (9, 128)])
+@pytest.mark.parametrize("idx,partition_size", [(3, 0), (4, 0), (4, 256), (6, 0), (8, 0), (9, 0), (9, 128), (10, 0)])
 def test_reused_work_list_across_layers_is_bit_identical(idx, partition_size):
     """The layers of one decode step share context lengths, tables and slots:
     the work list built by the first layer's call serves the others
@@ -436,7 +437,7 @@ def test_longest_contexts(dtype, Hq, Hkv, kernel, partition_size):
              label=f"long contexts {dtype} {kernel} partition={partition_size}")
 
 
-@pytest.mark.parametrize("idx", [3, 4, 5, 6, 8, 9])
+@pytest.mark.parametrize("idx", [3, 4, 5, 6, 8, 9, 10])
 def test_cache_policies_give_identical_bits(idx):
     """Streaming (nontemporal) and keeping (plain) key/value loads differ in
     speed only: both kernels, 16- and 8-bit caches, a window, split-K."""

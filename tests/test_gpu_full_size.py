@@ -26,7 +26,7 @@ def _sample(lay, k, rng):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8, 9])
+@pytest.mark.parametrize("idx", [2, 3, 4, 5, 6, 8, 9, 10])
 def test_full_size_sampled_rows(idx):
     cfg = CONFIGS[idx]
     lay = make_layout(cfg, seed=idx)

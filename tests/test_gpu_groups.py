@@ -1,8 +1,9 @@
 """GPU parity for any number G of query heads per KV head: groups that are no
-power of two (3, 5, 6, 7), single heads on the matrix cores, and groups
-larger than one workgroup computes (multi-query layers up to G = 71), cut
-into head chunks; both kernels, 16- and 8-bit caches, split-K and sliding
-windows, every row against the oracle."""
+power of two (3, 5, 6, 7), single heads on the matrix cores, several 16-head
+column tiles per workgroup, and groups larger than one workgroup computes
+(multi-query layers up to G = 128), cut into head chunks; both kernels, 16-
+and 8-bit caches, split-K and sliding windows, every row against the
+oracle."""
 import pytest
 import torch
 
@@ -23,14 +24,19 @@ GROUP_CASES = [
     ("f16", "same", 64, 16, 3, 1, "auto"),                  # 3
     ("bf16", "same", 128, 16, 2, 2, "mfma"),                # 1
     ("f16", "same", 128, 8, 4, 2, "mfma"),                  # 2
-    ("bf16", "same", 128, 32, 48, 2, "auto"),               # 24: 2 x 12
-    ("f16", "same", 128, 16, 32, 1, "auto"),                # 32: 2 x 16
-    ("bf16", "same", 64, 16, 71, 1, "auto"),                # 71: 4 x 15 + 11
+    ("bf16", "same", 128, 32, 48, 2, "auto"),               # 24: 2 column tiles
+    ("f16", "same", 128, 16, 32, 1, "auto"),                # 32: 2 column tiles
+    ("bf16", "same", 64, 16, 71, 1, "auto"),                # 71: 36 + 35 in 3 tiles
     ("bf16", "same", 128, 16, 10, 2, "valu"),               # 5 (vector kernel)
     ("f16", "same", 64, 8, 24, 1, "valu"),                  # 24: 3 x 8
     ("bf16", "fp8_e4m3", 128, 16, 10, 2, "auto"),           # 5, 8-bit cache
-    ("f16", "fp8_e4m3", 128, 32, 40, 1, "auto"),            # 40: 3 x 14, 8-bit cache
+    ("f16", "fp8_e4m3", 128, 32, 40, 1, "auto"),            # 40: 2 x 20 in 2 tiles, 8-bit cache
     ("bf16", "fp8_e4m3", 64, 16, 3, 1, "valu"),             # 3, 8-bit cache
+    ("f16", "same", 64, 32, 64, 1, "auto"),                 # 64: 4 column tiles
+    ("f16", "same", 64, 16, 128, 1, "auto"),                # 128: 2 x 64
+    ("bf16", "fp8_e4m3", 64, 16, 48, 1, "auto"),            # 48: 3 tiles, 8-bit cache
+    ("bf16", "same", 64, 8, 40, 2, "auto"),                 # 20, 8-token blocks: 2 x 10, one tile
+    ("bf16", "same", 128, 64, 24, 1, "mfma"),               # 24, 64-token blocks: 2 x 12
 ]
 
 
