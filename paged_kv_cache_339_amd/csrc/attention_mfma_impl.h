@@ -50,22 +50,34 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int DT> struct Mfma;
 
+// pack(a, b): two fp32 values rounded to nearest even into one dword (a in
+// the low half), one v_cvt_pk_{bf16,f16}_f32; kOne: 1.0 in both halves.
 template <> struct Mfma<PKV_BF16> {
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr uint32_t kOne = 0x3f803f80u;
   static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
                                                    __builtin_bit_cast(v8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_bf16(x); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), v2));
+  }
 };
 
 template <> struct Mfma<PKV_F16> {
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr uint32_t kOne = 0x3c003c00u;
   static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t narrow(float x) { return narrow_f16(x); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), v2));
+  }
 };
 
 // Four E4M3 codes (one dword) -> four 16-bit values of format DT (two dwords).
@@ -198,15 +210,19 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 
   const int Hkv = p.num_kv_heads, L = sw.L, t0 = sw.t0, N = p.num_blocks;
 
-  f32x4 o[T][DPL];
-  float m[T], l[T];
+  // l[ct][0]: running sum of the rounded weights of head 16 ct + r over
+  // every token so far (a product with an all-ones operand adds a chunk's
+  // 32 weights in one step; the other three entries are not used).
+  f32x4 o[T][DPL], l[T];
+  float m[T];
 #pragma unroll
   for (int ct = 0; ct < T; ++ct) {
 #pragma unroll
     for (int n = 0; n < DPL; ++n) o[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[ct] = -INFINITY;
-    l[ct] = 0.f;
+    l[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const u32x4 ones = u32x4{Ops::kOne, Ops::kOne, Ops::kOne, Ops::kOne};
   int bad = 0;
 
   const char* kbase = reinterpret_cast<const char*>(p.k_cache);
@@ -319,16 +335,13 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
         alpha[ct] = fast_exp2(m[ct] - ref);
         m[ct] = mn;
 
-        // Weights rounded to the operand format; the sum uses the rounded values.
-        float ps = 0.f;
+        // Weights rounded to the operand format; the sum adds the rounded
+        // values (in fp32, on the matrix core).
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t lo = Ops::narrow(fast_exp2(sc[2 * k] - ref));
-          const uint32_t hi = Ops::narrow(fast_exp2(sc[2 * k + 1] - ref));
-          pb[ct][k] = lo | (hi << 16);
-          ps += widen_half<DT>(pb[ct][k], false) + widen_half<DT>(pb[ct][k], true);
-        }
-        l[ct] = fmaf(l[ct], alpha[ct], ps);
+        for (int k = 0; k < 4; ++k)
+          pb[ct][k] = Ops::pack(fast_exp2(sc[2 * k] - ref), fast_exp2(sc[2 * k + 1] - ref));
+        l[ct][0] *= alpha[ct];
+        l[ct] = Ops::mma(ones, pb[ct], l[ct]);
       }
 
       // Value product: each transposed operand row serves every tile.
@@ -351,11 +364,6 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
     }
   }
 
-#pragma unroll
-  for (int ct = 0; ct < T; ++ct) {
-    l[ct] += shfl_xor_f(l[ct], 16);
-    l[ct] += shfl_xor_f(l[ct], 32);
-  }
   const int any_bad = __any(bad);
 
 #pragma unroll
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
         for (int i = 0; i < 4; ++i) sm.o[w][hr][DPL * (4 * q + i) + n] = o[ct][n][i];
       if (q == 0) {
         sm.m[w][hr] = m[ct];
-        sm.l[w][hr] = l[ct];
+        sm.l[w][hr] = l[ct][0];
       }
     }
   }
