@@ -344,6 +344,15 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
         l[ct] = Ops::mma(ones, pb[ct], l[ct]);
       }
 
+      // Rescale the accumulators of tiles whose running max grew (a factor
+      // of exactly 1 elsewhere: skipping it changes no bit).
+#pragma unroll
+      for (int ct = 0; ct < T; ++ct)
+        if (__any(alpha[ct] != 1.f)) {
+#pragma unroll
+          for (int n = 0; n < DPL; ++n) o[ct][n] *= alpha[ct];
+        }
+
       // Value product: each transposed operand row serves every tile.
       typename VRow<DPL>::type v16[8];
 #pragma unroll
@@ -356,10 +365,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
         for (int k = 0; k < 4; ++k)
           a[k] = __builtin_amdgcn_perm(v16[2 * k + 1][n >> 1], v16[2 * k][n >> 1], sel);
 #pragma unroll
-        for (int ct = 0; ct < T; ++ct) {
-          o[ct][n] *= alpha[ct];
-          o[ct][n] = Ops::mma(a, pb[ct], o[ct][n]);
-        }
+        for (int ct = 0; ct < T; ++ct) o[ct][n] = Ops::mma(a, pb[ct], o[ct][n]);
       }
     }
   }
