@@ -83,8 +83,6 @@ template <> struct Mfma<PKV_F16> {
 // Four E4M3 codes (one dword) -> four 16-bit values of format DT (two dwords).
 template <int DT>
 __device__ __forceinline__ u32x2 decode4_e4m3(uint32_t w) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   if constexpr (DT == PKV_BF16) {
     return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
@@ -388,7 +386,7 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
   }
   if (lane == 0) sm.bad[w] = any_bad;
   __syncthreads();
-  merge_and_store<DT, D, G, NW>(p, sm, it, sw.nparts);
+  merge_and_store<DT, D, G, NW, NT>(p, sm, it, sw.nparts);
 }
 
 // ---------------------------------------------------------------------------

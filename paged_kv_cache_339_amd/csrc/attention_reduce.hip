@@ -10,27 +10,40 @@
 namespace pkv {
 
 // One workgroup per (sequence, head chunk): the chunk's rows of a partition
-// are one contiguous run, read 4 elements per lane.  The merge runs over the
-// partitions in order, as online softmax:
+// are one contiguous run, read 8 elements (one 16-byte load of a 16-bit
+// row) per lane.  The merge runs over the partitions in order, as online
+// softmax:
 // M' = max(M, m_p), W = W 2^(M - M') + l_p 2^(m_p - M'), and O likewise with
 // l_p 2^(m_p - M') o_p; the result O / W equals the two-pass form above.
 constexpr int kReduceThreads = 256;
+constexpr int kReduceElems = 8;     // consecutive row elements per lane
+constexpr int kReduceAhead = 8;     // partitions whose loads are in flight together
 
-// Four consecutive partition-output elements (stored in the output format).
+// Eight consecutive partition-output elements (stored in the output format).
 template <int DT>
-__device__ __forceinline__ float4 load4(const void* base, size_t idx) {
+__device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8]) {
   if constexpr (DT == PKV_F32) {
-    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(reinterpret_cast<const float*>(base) + idx);
+    const f32x4v a = src[0], b = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
   } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    return make_float4(widen_half<DT>(w.x, false), widen_half<DT>(w.x, true),
-                       widen_half<DT>(w.y, false), widen_half<DT>(w.y, true));
+    const u32x4 w = load16(reinterpret_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wi = w[i];
+      x[2 * i] = widen_half<DT>(wi, false);
+      x[2 * i + 1] = widen_half<DT>(wi, true);
+    }
   }
 }
-constexpr int kReduceAhead = 4;     // partitions whose loads are in flight together
 
 template <int DT, int D>
 __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams p, int B) {
+  constexpr int E = kReduceElems;
   const int slots = p.num_kv_heads * p.chunks;
   const int s = blockIdx.x / slots;
   const int slot = blockIdx.x - s * slots;
@@ -41,20 +54,21 @@ __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams 
   if (sw.bad || sw.nparts <= 1) return;     // written by the main kernel
   const int G = p.cap;                      // rows per run in the workspace
   const size_t run0 = ((size_t)s * slots + slot) * p.max_parts;   // partition 0's first row is run0 * G
-  for (int e = threadIdx.x * 4; e < rows * D; e += blockDim.x * 4) {
+  for (int e = threadIdx.x * E; e < rows * D; e += blockDim.x * E) {
     const int g = e / D, d = e - g * D;
-    float M = -INFINITY, W = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    float M = -INFINITY, W = 0.f, O[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) O[k] = 0.f;
     for (int i0 = 0; i0 < sw.nparts; i0 += kReduceAhead) {
-      float m[kReduceAhead], l[kReduceAhead];
-      float4 o[kReduceAhead];
+      float m[kReduceAhead], l[kReduceAhead], o[kReduceAhead][E];
 #pragma unroll
       for (int k = 0; k < kReduceAhead; ++k) {
         const int i = min(i0 + k, sw.nparts - 1);
         const size_t row = (run0 + i) * G + g;
-        m[k] = p.ws_ml[row * 2];
-        l[k] = p.ws_ml[row * 2 + 1];
-        o[k] = load4<DT>(p.ws_o, row * D + d);
+        const f32x2v ml = *reinterpret_cast<const f32x2v*>(p.ws_ml + row * 2);
+        m[k] = ml[0];
+        l[k] = ml[1];
+        load8<DT>(p.ws_o, row * D + d, o[k]);
       }
 #pragma unroll
       for (int k = 0; k < kReduceAhead; ++k) {
@@ -64,18 +78,15 @@ __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams 
         const float a = fast_exp2(M - ref);
         const float b = l[k] * fast_exp2(m[k] - ref);
         W = fmaf(W, a, b);
-        O.x = fmaf(O.x, a, o[k].x * b);
-        O.y = fmaf(O.y, a, o[k].y * b);
-        O.z = fmaf(O.z, a, o[k].z * b);
-        O.w = fmaf(O.w, a, o[k].w * b);
+#pragma unroll
+        for (int j = 0; j < E; ++j) O[j] = fmaf(O[j], a, o[k][j] * b);
         M = Mn;
       }
     }
-    const size_t out0 = ((size_t)s * p.num_q_heads + q0 + g) * D + d;
-    store_elem<DT>(p.out, out0, O.x / W);
-    store_elem<DT>(p.out, out0 + 1, O.y / W);
-    store_elem<DT>(p.out, out0 + 2, O.z / W);
-    store_elem<DT>(p.out, out0 + 3, O.w / W);
+    float r[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) r[j] = O[j] / W;
+    store_row8<DT, false>(p.out, ((size_t)s * p.num_q_heads + q0 + g) * D + d, r);
   }
 }
 
@@ -83,8 +94,8 @@ namespace {
 template <int DT, int D>
 hipError_t launch_reduce(const AttnParams& p, int B, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.chunks));
-  // Lanes take 4 elements each; small groups need fewer lanes.
-  const int rows = p.chunk_rows * D / 4;
+  // Lanes take 8 elements each; small groups need fewer lanes.
+  const int rows = p.chunk_rows * D / kReduceElems;
   const int threads = min(kReduceThreads, max(kWave, (rows + kWave - 1) / kWave * kWave));
   hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(threads), 0, st, p, B);
   return hipGetLastError();

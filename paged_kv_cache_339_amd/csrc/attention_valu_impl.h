@@ -218,7 +218,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
     sm.bad[w] = __any(bad);
   }
   __syncthreads();
-  merge_and_store<DT, D, G, NW>(p, sm, it, sw.nparts);
+  merge_and_store<DT, D, G, NW, NT>(p, sm, it, sw.nparts);
 }
 
 // ---------------------------------------------------------------------------
