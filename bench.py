@@ -6,7 +6,10 @@ workload has copy-on-write pairs, then pkv_decode_step, which stores the
 token each sequence appends (reshape_and_cache) in the launch that builds
 the attention work list, and runs paged decode attention over all cached
 tokens (main kernel, plus the split-K reduce when partitions split a
-sequence).  Inputs are synthetic, seeded, N(0, 1), and
+sequence).  On the shared-prefix workload the step is copy_blocks,
+reshape_and_cache and pkv_paged_attention_decode_shared_prefix, which reads
+each prompt's shared blocks once for all its samples (--per-sample-prefix:
+the plain decode step instead).  Inputs are synthetic, seeded, N(0, 1), and
 resident in HBM before timing starts.  The default workload is a
 Llama-2-7B-shaped layer: batch 64, 32 heads, head_dim 128, fp16 KV cache in
 16-token blocks, context lengths uniform in [128, 2048], blocks scattered at
@@ -20,7 +23,9 @@ Prints ONE JSON line:
                second pass on the kernel's stream: K launches of the main
                kernel alone, back to back between two HIP events (the work
                list of the first pass reused), or, when a split-K reduce
-               follows it, events right before and after it in K steps
+               follows it (and on the shared-prefix call, for its pass over
+               each sequence's own tokens), events right before and after it
+               in K steps
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
                on this host's cores (a reported baseline, not the target)
 
@@ -503,6 +508,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--per-sample-prefix", action="store_true",
+                    help="shared-prefix workloads: read the shared prompt blocks once per sample (plain decode "
+                         "step, cache-resident re-reads) instead of once per prompt for all its samples "
+                         "(pkv_paged_attention_decode_shared_prefix, the default)")
     ap.add_argument("--swap", action="store_true",
                     help="instead of the decode step, time pkv_swap_blocks of a quarter of the workload's "
                          "blocks to a pinned host pool and back (PCIe-bound)")
@@ -545,6 +554,19 @@ def main():
     if args.cache_policy and args.cache_policy != cfg.cache_policy:
         cfg = cfg.scaled(cache_policy=args.cache_policy)
         tag += f"_{args.cache_policy}"
+    if args.per_sample_prefix and cfg.lengths != "shared_prefix":
+        sys.exit("--per-sample-prefix needs a shared-prefix workload")
+    grouped = cfg.lengths == "shared_prefix" and not args.per_sample_prefix
+    if args.per_sample_prefix:
+        tag += "_persample"
+    if grouped:
+        # The prefix is read once per group: no partition at the prompt's end
+        # and no cache-resident re-reads are needed.
+        if args.partition_size < 0:
+            part = 0
+        if not args.cache_policy:
+            cfg = cfg.scaled(cache_policy="stream")
+        cfg = cfg.scaled(partition_size=part)
     if part != cfg.partition_size:
         tag += f"_partition{part or 'auto'}"
     seed = args.config if args.seed is None else args.seed
@@ -588,6 +610,14 @@ def main():
     max_ctx = layout.max_context_len
     ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code, part, args.kernel, cfg.sliding_window,
                                    cfg.kv_format, cfg.k_scale, cfg.v_scale)
+    if grouped:
+        from synthetic import shared_prefix_groups
+        members_np, prefix_np = shared_prefix_groups(layout)
+        members, prefix_lens = ints(members_np), ints(prefix_np)
+        Gn, Gs, max_prefix = members_np.shape[0], members_np.shape[1], int(prefix_np.max())
+        ws_bytes = pkv.shared_prefix_workspace_bytes(S, Hq, Hkv, D, B, max_ctx, Gn, Gs, max_prefix, code, part,
+                                                     args.kernel, cfg.kv_format, cfg.k_scale, cfg.v_scale,
+                                                     cfg.cache_policy)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
@@ -612,6 +642,19 @@ def main():
                 vp(lens.data_ptr()), cfg.scale, B, Hkv, S, Hq, D, layout.block_tables.shape[1], max_ctx,
                 layout.num_blocks, code, vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream))
 
+    def grouped_args(opts):
+        """pkv_paged_attention_decode_shared_prefix over the caches as the steps left them."""
+        return (vp(out.data_ptr()), vp(q.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()), vp(tables.data_ptr()),
+                vp(lens.data_ptr()), vp(prefix_lens.data_ptr()), vp(members.data_ptr()), Gn, Gs, max_prefix,
+                cfg.scale, B, Hkv, S, Hq, D, layout.block_tables.shape[1], max_ctx, layout.num_blocks, code,
+                vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream))
+
+    if grouped:
+        step_args = grouped_args      # noqa: F811  (the step's attention call)
+
+    scatter_args = (vp(kn.data_ptr()), vp(vn.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()), vp(slots.data_ptr()),
+                    S, Hkv, D, B, layout.num_blocks, code, vp(stream))
+
     K, W = args.steps, args.warmup
     win = cfg.sliding_window
     kvf = KV_FORMATS[cfg.kv_format]
@@ -625,7 +668,14 @@ def main():
         if copy_args is not None:
             st = lib.pkv_copy_blocks(*copy_args)
             assert st == 0, st
-        st = lib.pkv_decode_step(*a)
+        if grouped:
+            # The new tokens' store, then attention with each prompt's shared
+            # blocks read once for its samples.
+            st = lib.pkv_reshape_and_cache(*scatter_args)
+            assert st == 0, st
+            st = lib.pkv_paged_attention_decode_shared_prefix(*a)
+        else:
+            st = lib.pkv_decode_step(*a)
         assert st == 0, st
 
     for _ in range(W):
@@ -648,7 +698,7 @@ def main():
     # it runs K times back to back on the work list pass 1 left in the
     # workspace (reuse_plan), between two events; with one, events go right
     # before and after the main kernel inside each of K more steps.
-    if parts_per_seq == 1:
+    if parts_per_seq == 1 and not grouped:
         reuse = AttnOptions(part, KERNELS[args.kernel], None, None, win, kvf, cfg.k_scale, cfg.v_scale, 1, cp)
         dec = decode_args(reuse)
         m0, m1 = ev.create(), ev.create()
@@ -669,6 +719,8 @@ def main():
         torch.cuda.synchronize()
         main_ms = [ev.ms(begins[i], ends[i]) for i in range(K)]
         main_timing = "events right before and after the main kernel in each of K steps"
+        if grouped:
+            main_timing += " (the pass over each sequence's own tokens)"
     ev.close()
     assert torch.isfinite(out.float()).all().item(), "non-finite attention output"
 
@@ -678,6 +730,20 @@ def main():
     first = np.maximum(0, lens64 - win) // B if win > 0 else np.zeros_like(lens64)
     nblk = -(-lens64 // B) - first                    # table entries read per (sequence, KV head)
     alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4   # es: q / out format
+    extra = {}
+    if grouped:
+        # The timed kernel is the pass over each sequence's own tokens
+        # [P_s, L_s); the shared prefixes are read by the grouped pass.
+        kvs = DTYPE_BYTES[cfg.kv_dtype]
+        own = lens64 - prefix_np
+        own_blk = -(-lens64 // B) - prefix_np // B
+        alg_bytes = int(own.sum()) * Hkv * D * 2 * kvs + 2 * S * Hq * D * es + int(own_blk.sum()) * 4 * Hkv + S * 8
+        pre_tokens = int(prefix_np[members_np[:, 0]].sum())
+        extra = {"grouped_prefix": {
+            "groups": Gn, "members": Gs, "prefix_tokens": int(prefix_np[0]),
+            "unique_kv_bytes_per_step": (pre_tokens + int(own.sum())) * Hkv * D * 2 * kvs,
+            "prefix_pass_kv_bytes": pre_tokens * Hkv * D * 2 * kvs,
+            "own_pass_kv_bytes": int(own.sum()) * Hkv * D * 2 * kvs}}
     achieved = alg_bytes / main_s / 1e9
     kv_gbps = step_kv / step_s / 1e9
     result = {
@@ -701,8 +767,11 @@ def main():
             "kv_bytes_per_step": step_kv, "partition_size": part, "partition_tokens": chosen_part,
             "partitions_per_seq": parts_per_seq, "kernel": kernel_used,
             "sliding_window": win, "kv_format": cfg.kv_format, "cache_policy": cfg.cache_policy,
-            "step": ("copy_blocks + " if copy_args else "") + "decode_step (new-token store + plan, attention)",
+            "step": ("copy_blocks + " if copy_args else "") + (
+                "reshape_and_cache + decode_shared_prefix (grouped prefix pass, own-token pass, merge)" if grouped
+                else "decode_step (new-token store + plan, attention)"),
         },
+        **extra,
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
         "seq_heads_per_s": round(S * Hq / step_s, 1),
         "attention_main_us": round(main_s * 1e6, 2),

@@ -251,6 +251,59 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
                     pkv_dtype dtype, void* workspace, size_t workspace_bytes,
                     const pkv_attn_options* opts, void* stream);
 
+/*
+ * Decode attention for groups of sequences that share the first blocks of
+ * their tables: the parallel samples of one prompt, or beams, whose common
+ * prefix blocks the block manager shares by reference count ("pagedattention
+ * vllm" glossary, Copy-on-Write Sharing: Prefix Sharing, Reference Counting
+ * and Use Cases; "What is PagedAttention" (tecyfy), What it changes).  The output is that of
+ * pkv_paged_attention_decode on the same arguments (the same softmax over
+ * t in [0, L) of every sequence); only the reads differ: the shared prefix
+ * is read once per group instead of once per member.
+ *
+ * group_members: device int32 [num_groups, group_size]: sequence indices,
+ *   -1 for an unused slot; a sequence appears in at most one group.
+ * prefix_lens: device int32 [num_seqs]: P_s, the tokens at the start of
+ *   sequence s whose keys and values are the same for every member of its
+ *   group (the same physical blocks); all members of a group give the same
+ *   P, with 0 <= P <= L_s, and sequences in no group give 0.  Tokens
+ *   [0, P) of a group are read through the table of its first member.
+ * max_prefix_len (host): >= every prefix_lens[s], <= max_context_len and
+ *   <= max_blocks_per_seq * block_size; it sizes the prefix launch.
+ *
+ * Launches, in stream order: a gather of each group's member queries (and
+ * its first member's table row and prefix length) into the workspace; the
+ * decode kernels on the groups, whose G members x g heads per KV head form
+ * a query group of G g heads (matrix cores for 16-bit data), giving each
+ * member's prefix part and its log-denominator; the decode kernels on the
+ * whole batch over t in [P_s, L_s); a merge of the two parts
+ *   out = (o_a 2^(l_a - m) + o_b 2^(l_b - m)) / (2^(l_a - m) + 2^(l_b - m)),
+ * m = max(l_a, l_b), where l is log2 of a part's softmax denominator in
+ * units of log2(e) * scale * <q, k>.  The parts are rounded to the output
+ * format before the merge (one more rounding than the plain call).
+ * Arguments that break the rules above give undefined rows but stay
+ * memory-safe; a data error (table entry, length) makes the affected rows
+ * NaN as in pkv_paged_attention_decode.
+ * opts: as pkv_paged_attention_decode, except sliding_window (must be 0:
+ * PKV_ERR_UNSUPPORTED) and kernel and the events, which apply to the
+ * whole-batch pass only.  workspace: at least
+ * pkv_paged_attention_shared_prefix_workspace_bytes bytes, 16-byte aligned.
+ * num_groups = 0 is a plain decode.
+ */
+size_t pkv_paged_attention_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t num_groups, int32_t group_size,
+    int32_t max_prefix_len, pkv_dtype dtype, const pkv_attn_options* opts);
+
+int pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* prefix_lens,
+    const int32_t* group_members, int32_t num_groups, int32_t group_size, int32_t max_prefix_len,
+    float scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+    int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
+    pkv_dtype dtype, void* workspace, size_t workspace_bytes, const pkv_attn_options* opts,
+    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Cache write and copy-on-write                                             */
 /* ------------------------------------------------------------------------ */

@@ -20,14 +20,17 @@ from .ops import (
     decode_step,
     gather_kv,
     paged_attention_decode,
+    paged_attention_decode_shared_prefix,
     plan_info,
     reshape_and_cache,
     reshape_and_cache_fp8,
+    shared_prefix_workspace_bytes,
     swap_blocks,
     workspace_bytes,
 )
 
 __all__ = [
     "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
-    "paged_attention_decode", "plan_info", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
+    "paged_attention_decode", "paged_attention_decode_shared_prefix", "plan_info", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
+    "shared_prefix_workspace_bytes",
 ]

@@ -53,6 +53,11 @@ def load(path: str = LIB_PATH):
         "pkv_paged_attention_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32,
                                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                                       c_vp, c_size, ctypes.POINTER(AttnOptions), c_vp]),
+        "pkv_paged_attention_shared_prefix_workspace_bytes": (
+            c_size, [c_i32] * 9 + [ctypes.c_int, ctypes.POINTER(AttnOptions)]),
+        "pkv_paged_attention_decode_shared_prefix": (
+            ctypes.c_int, [c_vp] * 8 + [c_i32, c_i32, c_i32, c_f32] + [c_i32] * 8 + [ctypes.c_int, c_vp, c_size,
+                                                                             ctypes.POINTER(AttnOptions), c_vp]),
         "pkv_decode_step": (ctypes.c_int, [c_vp] * 9 + [c_f32] + [c_i32] * 8 + [ctypes.c_int, c_vp, c_size,
                                                                               ctypes.POINTER(AttnOptions), c_vp]),
         "pkv_reshape_and_cache": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,

@@ -270,7 +270,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
                 int32_t num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append) {
+                const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append,
+                const int32_t* seq_start = nullptr, float* lse = nullptr) {
   Plan plan;
   const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, dtype, opts, &plan);
@@ -313,6 +314,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.chunk_rows = plan.chunk_rows;
   p.cap = plan.cap;
   p.items = (int32_t)((int64_t)num_seqs * num_kv_heads * plan.max_parts);
+  p.seq_start = seq_start;
+  p.lse = lse;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_pending_error();
@@ -403,6 +406,155 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                      num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                      max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts, stream, &a);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of a shared-prefix call: the virtual batch (queries, tables,
+// lengths, outputs and log-denominators), the real batch's log-denominators,
+// then the workspaces of the two decode passes.
+struct PrefixLayout {
+  int32_t tab_v;
+  size_t q_v, tables_v, lens_v, o_v, lse_v, lse_t, ws_pre, ws_suf, bytes;
+  size_t ws_pre_bytes, ws_suf_bytes;
+  pkv_attn_options pre, suf;
+};
+
+int prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t max_context_len, int32_t num_groups,
+                  int32_t group_size, int32_t max_prefix_len, pkv_dtype dtype,
+                  const pkv_attn_options* opts, PrefixLayout* L) {
+  pkv_attn_options o{};
+  if (opts) o = *opts;
+  if (o.sliding_window != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_groups < 0 || max_prefix_len < 0 || max_prefix_len > max_context_len) return PKV_ERR_SHAPE;
+  if (num_groups > 0 && group_size <= 0) return PKV_ERR_SHAPE;
+  if (num_groups == 0) group_size = 1;
+  const int64_t vheads = (int64_t)num_q_heads * group_size;
+  if (vheads > 0x7fffffff || (int64_t)num_groups * group_size > 0x7fffffff) return PKV_ERR_SHAPE;
+  L->suf = o;
+  L->pre = o;
+  L->pre.kernel = PKV_KERNEL_AUTO;       // the virtual batch is grouped-query
+  L->pre.main_begin_event = L->pre.main_end_event = nullptr;
+  Plan suf, pre;
+  int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                     dtype, &L->suf, &suf);
+  if (st != PKV_OK) return st;
+  st = make_plan(num_groups, (int32_t)vheads, num_kv_heads, head_dim, block_size, max_prefix_len,
+                 dtype, &L->pre, &pre);
+  if (st != PKV_OK) return st;
+  L->tab_v = max_prefix_len > 0 ? (max_prefix_len + block_size - 1) / block_size : 1;
+  const size_t es = (size_t)dtype_bytes(dtype);
+  const size_t vrows = (size_t)num_groups * (size_t)vheads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  L->q_v = take(vrows * head_dim * es);
+  L->tables_v = take((size_t)num_groups * L->tab_v * sizeof(int32_t));
+  L->lens_v = take((size_t)num_groups * sizeof(int32_t));
+  L->o_v = take(vrows * head_dim * es);
+  L->lse_v = take(vrows * sizeof(float));
+  L->lse_t = take((size_t)num_seqs * num_q_heads * sizeof(float));
+  L->ws_pre_bytes = pre.ws_bytes;
+  L->ws_suf_bytes = suf.ws_bytes;
+  L->ws_pre = take(pre.ws_bytes);
+  L->ws_suf = take(suf.ws_bytes);
+  L->bytes = num_seqs > 0 ? off : 0;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_paged_attention_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_context_len, int32_t num_groups, int32_t group_size,
+    int32_t max_prefix_len, pkv_dtype dtype, const pkv_attn_options* opts) {
+  PrefixLayout L;
+  if (prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                    num_groups, group_size, max_prefix_len, dtype, opts, &L) != PKV_OK)
+    return 0;
+  return L.bytes;
+}
+
+int pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* prefix_lens,
+    const int32_t* group_members, int32_t num_groups, int32_t group_size, int32_t max_prefix_len,
+    float scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+    int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks,
+    pkv_dtype dtype, void* workspace, size_t workspace_bytes, const pkv_attn_options* opts,
+    void* stream) {
+  PrefixLayout L;
+  int st = prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_context_len, num_groups, group_size, max_prefix_len, dtype, opts, &L);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (num_groups > 0 && (!prefix_lens || !group_members)) return PKV_ERR_NULL;
+  // Every check of the two decode passes is made here, before the first launch.
+  if (max_blocks_per_seq <= 0 || L.tab_v > max_blocks_per_seq || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t vheads = num_q_heads * (num_groups > 0 ? group_size : 1);
+  if (num_groups > 0) {
+    pkv::PrefixArgs a;
+    a.q = static_cast<const char*>(q);
+    a.q_v = ws + L.q_v;
+    a.tables = block_tables;
+    a.tables_v = reinterpret_cast<int32_t*>(ws + L.tables_v);
+    a.prefix_lens = prefix_lens;
+    a.lens_v = reinterpret_cast<int32_t*>(ws + L.lens_v);
+    a.members = group_members;
+    a.num_seqs = num_seqs;
+    a.num_groups = num_groups;
+    a.group_size = group_size;
+    a.q_heads = num_q_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.row_pieces = head_dim * dtype_bytes(dtype) / 16;
+    a.max_blocks = max_blocks_per_seq;
+    a.tab_v = L.tab_v;
+    clear_pending_error();
+    const hipError_t e = pkv::launch_prefix_prep(a, s);
+    if (e != hipSuccess) return launch_status(e);
+    st = decode_impl(ws + L.o_v, ws + L.q_v, k_cache, v_cache, a.tables_v, a.lens_v, scale,
+                     block_size, num_kv_heads, num_groups, vheads, head_dim, L.tab_v,
+                     max_prefix_len, num_blocks, dtype, ws + L.ws_pre, L.ws_pre_bytes, &L.pre,
+                     stream, nullptr, nullptr, reinterpret_cast<float*>(ws + L.lse_v));
+    if (st != PKV_OK) return st;
+  }
+  st = decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                   num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                   max_context_len, num_blocks, dtype, ws + L.ws_suf, L.ws_suf_bytes, &L.suf,
+                   stream, nullptr, num_groups > 0 ? prefix_lens : nullptr,
+                   reinterpret_cast<float*>(ws + L.lse_t));
+  if (st != PKV_OK || num_groups == 0) return st;
+  pkv::PrefixMergeArgs m;
+  m.out = out;
+  m.lse = reinterpret_cast<const float*>(ws + L.lse_t);
+  m.o_v = ws + L.o_v;
+  m.lse_v = reinterpret_cast<const float*>(ws + L.lse_v);
+  m.members = group_members;
+  m.num_seqs = num_seqs;
+  m.num_groups = num_groups;
+  m.group_size = group_size;
+  m.q_heads = num_q_heads;
+  m.group = num_q_heads / num_kv_heads;
+  hipError_t err = hipSuccess;
+  clear_pending_error();
+  if (!pkv::launch_prefix_merge(m, dtype, head_dim, s, &err)) return PKV_ERR_UNSUPPORTED;
+  return launch_status(err);
 }
 
 int pkv_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,

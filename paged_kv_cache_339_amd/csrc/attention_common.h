@@ -36,6 +36,11 @@ __device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
           (int64_t)raw > (int64_t)p.max_blocks_per_seq * B;
   w.L = w.bad ? 0 : raw;
   w.t0 = (p.window > 0 && w.L > p.window) ? w.L - p.window : 0;
+  if (p.seq_start != nullptr) {
+    const int st = p.seq_start[s];
+    if (st > w.t0) w.t0 = st;
+    if (w.t0 >= w.L) w.L = w.t0 = 0;     // nothing left to attend to
+  }
   w.blk0 = w.t0 / B;
   w.nblk = w.L > 0 ? (w.L + B - 1) / B - w.blk0 : 0;
   w.nparts = (w.nblk + p.part_blocks - 1) / p.part_blocks;
@@ -87,13 +92,17 @@ __device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
   return it;
 }
 
-// Rows that cannot be computed (data error) become NaN; empty sequences 0.
+// Rows that cannot be computed (data error) become NaN, with a NaN
+// log-denominator; empty sequences 0, with -inf.
 template <int DT, int D, int NT>
 __device__ __forceinline__ void fill_rows(const AttnParams& p, const WorkItem& it, float value) {
   for (int idx = threadIdx.x; idx < it.rows * D; idx += NT) {
     const int g = idx / D, d = idx % D;
     store_elem<DT>(p.out, ((size_t)it.s * p.num_q_heads + it.q0 + g) * D + d, value);
   }
+  if (p.lse != nullptr)
+    for (int g = threadIdx.x; g < it.rows; g += NT)
+      p.lse[(size_t)it.s * p.num_q_heads + it.q0 + g] = value == 0.f ? -INFINITY : value;
 }
 
 // LDS staging for the cross-wave merge.
@@ -132,6 +141,28 @@ __device__ __forceinline__ void store_row8(void* base, size_t idx, const float (
     u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + idx);
     if constexpr (NTS) __builtin_nontemporal_store(w, dst);
     else *dst = w;
+  }
+}
+
+// Eight consecutive elements of a row stored in format DT, widened to fp32.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8]) {
+  if constexpr (DT == PKV_F32) {
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(reinterpret_cast<const float*>(base) + idx);
+    const f32x4v a = src[0], b = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  } else {
+    const u32x4 w = load16(reinterpret_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wi = w[i];
+      x[2 * i] = widen_half<DT>(wi, false);
+      x[2 * i + 1] = widen_half<DT>(wi, true);
+    }
   }
 }
 
@@ -177,6 +208,8 @@ __device__ __forceinline__ void merge_and_store(const AttnParams& p, const Merge
     for (int e = 0; e < V; ++e) r[e] = bad ? __builtin_nanf("") : o[e] / tot * p.v_scale;
     if (nparts == 1) {
       store_row8<DT, false>(p.out, ((size_t)it.s * p.num_q_heads + it.q0 + g) * D + d, r);
+      if (p.lse != nullptr && d == 0)
+        p.lse[(size_t)it.s * p.num_q_heads + it.q0 + g] = bad ? __builtin_nanf("") : M + log2f(tot);
     } else {
       const size_t row0 =
           (((size_t)it.s * p.num_kv_heads * p.chunks + it.slot) * p.max_parts + it.part) * G;

@@ -19,28 +19,6 @@ constexpr int kReduceThreads = 256;
 constexpr int kReduceElems = 8;     // consecutive row elements per lane
 constexpr int kReduceAhead = 8;     // partitions whose loads are in flight together
 
-// Eight consecutive partition-output elements (stored in the output format).
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8]) {
-  if constexpr (DT == PKV_F32) {
-    const f32x4v* src = reinterpret_cast<const f32x4v*>(reinterpret_cast<const float*>(base) + idx);
-    const f32x4v a = src[0], b = src[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = a[i];
-      x[4 + i] = b[i];
-    }
-  } else {
-    const u32x4 w = load16(reinterpret_cast<const uint16_t*>(base) + idx);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t wi = w[i];
-      x[2 * i] = widen_half<DT>(wi, false);
-      x[2 * i + 1] = widen_half<DT>(wi, true);
-    }
-  }
-}
-
 template <int DT, int D>
 __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams p, int B) {
   constexpr int E = kReduceElems;
@@ -87,6 +65,7 @@ __global__ __launch_bounds__(kReduceThreads) void attn_reduce_kernel(AttnParams 
 #pragma unroll
     for (int j = 0; j < E; ++j) r[j] = O[j] / W;
     store_row8<DT, false>(p.out, ((size_t)s * p.num_q_heads + q0 + g) * D + d, r);
+    if (p.lse != nullptr && d == 0) p.lse[(size_t)s * p.num_q_heads + q0 + g] = M + log2f(W);
   }
 }
 

@@ -53,6 +53,12 @@ struct AttnParams {
   int32_t chunk_rows;         // R
   int32_t cap;                // rows per (sequence, chunk, partition) in the workspace
   int32_t items;              // S * Hkv * max_parts, work items per chunk
+  // Optional (nullptr = none): first attended token of each sequence [S]
+  // (tokens before it are skipped as before a sliding window), and the
+  // log2 of each output row's softmax denominator [S, Hq], in the units of
+  // scale_log2: log2 sum_t 2^(scale_log2 <q, k_t>) (-inf for an empty row).
+  const int32_t* seq_start;
+  float* lse;
 };
 
 // Workgroups of a main-kernel launch: one per work item and head chunk;
@@ -104,6 +110,32 @@ hipError_t launch_append_and_plan(const AttnParams& p, int block_size, const App
                                   hipStream_t stream);
 bool launch_attention_reduce(const AttnParams& p, pkv_dtype dt, int head_dim, int block_size,
                              hipStream_t stream, hipError_t* err);
+
+// Shared-prefix decode: the prep launch (virtual queries, tables, lengths
+// of each group) and the merge of prefix and suffix parts.
+struct PrefixArgs {
+  const char* q;              // [S, Hq, D] query rows
+  char* q_v;                  // [Gn, Hq * Gs, D] virtual query rows (workspace)
+  const int32_t* tables;      // [S, M]
+  int32_t* tables_v;          // [Gn, Mv] (workspace)
+  const int32_t* prefix_lens; // [S]
+  int32_t* lens_v;            // [Gn] (workspace)
+  const int32_t* members;     // [Gn, Gs], -1 = unused slot
+  int32_t num_seqs, num_groups, group_size, q_heads, group, row_pieces, max_blocks, tab_v;
+};
+
+struct PrefixMergeArgs {
+  void* out;                  // [S, Hq, D]: the suffix parts on entry, the results on exit
+  const float* lse;           // [S, Hq] log2-denominators of the suffix parts
+  const void* o_v;            // [Gn, Hq * Gs, D] prefix parts of the virtual batch
+  const float* lse_v;         // [Gn, Hq * Gs]
+  const int32_t* members;     // [Gn, Gs]
+  int32_t num_seqs, num_groups, group_size, q_heads, group;
+};
+
+hipError_t launch_prefix_prep(const PrefixArgs& a, hipStream_t stream);
+bool launch_prefix_merge(const PrefixMergeArgs& a, pkv_dtype dt, int head_dim, hipStream_t stream,
+                         hipError_t* err);
 
 hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
                                         const int32_t* slot_mapping, int32_t num_tokens,

@@ -148,6 +148,57 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                  num_groups, group_size, max_prefix_len, dtype_code_, partition_size=0,
+                                  kernel="auto", kv_format="same", k_scale=1.0, v_scale=1.0, cache_policy="stream"):
+    opts = _options(partition_size, kernel, None, 0, kv_format, k_scale, v_scale, False, cache_policy)
+    return int(lib.pkv_paged_attention_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, num_groups, group_size,
+        max_prefix_len, dtype_code_, ctypes.byref(opts)))
+
+
+def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, prefix_lens,
+                                         group_members, max_prefix_len, scale, block_size, num_kv_heads,
+                                         max_context_len, partition_size=0, kernel="auto", workspace=None,
+                                         stream=None, main_events=None, kv_format="same", k_scale=1.0,
+                                         v_scale=1.0, reuse_plan=False, cache_policy="stream"):
+    """paged_attention_decode for groups of sequences whose first
+    prefix_lens[s] tokens are the same blocks (parallel samples of a prompt,
+    beams): each group's shared prefix is read once for all its members.
+
+    group_members: int32 [num_groups, group_size] sequence indices (-1 =
+    unused slot); prefix_lens: int32 [S], equal within a group, 0 outside any
+    group, <= the sequence's length; max_prefix_len: host int >= every
+    prefix_lens[s].  Other arguments as paged_attention_decode."""
+    if reuse_plan and workspace is None:
+        raise ValueError("reuse_plan needs the workspace of the call that built the work lists")
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                            kv_format)
+    if group_members.dim() != 2:
+        raise ValueError("group_members must be [num_groups, group_size]")
+    if prefix_lens.shape != (S,):
+        raise ValueError("prefix_lens must be [num_seqs]")
+    Gn, Gs = group_members.shape
+    code = dtype_code(q)
+    if workspace is None:
+        need = shared_prefix_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, Gn, Gs, max_prefix_len, code,
+                                             partition_size, kernel, kv_format, k_scale, v_scale, cache_policy)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    opts = _options(partition_size, kernel, main_events, 0, kv_format, k_scale, v_scale, reuse_plan, cache_policy)
+    st = lib.pkv_paged_attention_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(prefix_lens, "prefix_lens", torch.int32), _dev(group_members, "group_members", torch.int32),
+        Gn, Gs, int(max_prefix_len), float(scale), B, Hkv, S, Hq, D, block_tables.shape[1],
+        int(max_context_len), N, code, *_ws_args(workspace), ctypes.byref(opts), _stream(stream))
+    check(st, "paged_attention_decode_shared_prefix")
+    return out
+
+
 def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale,
                 block_size, num_kv_heads, max_context_len, partition_size=0, kernel="auto", workspace=None,
                 stream=None, main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,

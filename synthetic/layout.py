@@ -149,3 +149,18 @@ def make_layout(cfg: DecodeConfig, seed: int, lengths=None) -> Layout:
                   pool_order=order, used_blocks=cursor, new_slots=new_slots, live=live,
                   cow_pairs=np.array(pairs, dtype=np.int32).reshape(-1, 2),
                   cow_rows=(cfg.prompt_len % B) if shared else 0)
+
+
+def shared_prefix_groups(layout: Layout):
+    """Groups of a shared-prefix layout and their shared tokens.
+
+    Returns (members int32 [prompts, samples], prefix_lens int32 [S]): the
+    samples of each prompt, and for every sequence the prompt tokens held in
+    whole blocks that all samples of the prompt share (the partial last
+    prompt block is a private copy after the copy-on-write)."""
+    cfg = layout.cfg
+    S = len(layout.context_lens)
+    spp = cfg.samples_per_prompt
+    members = np.arange(S, dtype=np.int32).reshape(S // spp, spp)
+    prefix = np.full(S, (cfg.prompt_len // cfg.block_size) * cfg.block_size, dtype=np.int32)
+    return members, prefix

@@ -258,3 +258,54 @@ def test_cache_policy_values():
                                                    None)
         assert st == (0 if policy in (0, 1) else -2), policy
     assert sizes[0] == sizes[1] > 0 and sizes[2] == sizes[3] == 0
+
+
+def shared(**over):
+    """pkv_paged_attention_decode_shared_prefix with fake pointers: only calls
+    that fail a host check are made."""
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, prefix=FAKE, members=FAKE, Gn=2, Gs=4,
+             max_prefix=32, scale=0.125, B=16, Hkv=2, S=8, Hq=2, D=64, M=4, max_ctx=64, N=32, dtype=0,
+             ws=None, ws_bytes=0, opts=None, stream=None)
+    a.update(over)
+    return pkv.lib.pkv_paged_attention_decode_shared_prefix(
+        a["out"], a["q"], a["k"], a["v"], a["tables"], a["lens"], a["prefix"], a["members"], a["Gn"], a["Gs"],
+        a["max_prefix"], a["scale"], a["B"], a["Hkv"], a["S"], a["Hq"], a["D"], a["M"], a["max_ctx"], a["N"],
+        a["dtype"], a["ws"], a["ws_bytes"], a["opts"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(members=None), -1), (dict(prefix=None), -1), (dict(out=None), -1),
+    (dict(max_prefix=65), -2), (dict(max_prefix=-1), -2), (dict(Gn=-1), -2), (dict(Gs=0), -2),
+    (dict(max_prefix=64, M=3), -2),                        # prefix rows longer than a table row
+    (dict(opts=ctypes.byref(AttnOptions(0, 0, None, None, 16))), -4),   # no sliding window
+    (dict(q=ctypes.c_void_p(0x1008)), -5), (dict(), -6), (dict(ws=FAKE, ws_bytes=64), -6),
+    (dict(D=96), -4), (dict(Hq=3), -2)])
+def test_shared_prefix_rejects(over, status):
+    assert shared(**over) == status
+
+
+def test_shared_prefix_without_groups_needs_no_prefix_arrays():
+    # num_groups = 0 is a plain decode: prefix_lens and group_members may be NULL.
+    assert shared(Gn=0, Gs=0, prefix=None, members=None, max_prefix=0) == -6   # gets to the workspace check
+    assert shared(S=0, out=None, q=None) == 0
+
+
+def test_shared_prefix_workspace_sizes():
+    """The virtual batch (queries, tables, lengths, outputs, log-denominators),
+    the real batch's log-denominators, then the two passes' workspaces."""
+    sp, ws = pkv.shared_prefix_workspace_bytes, pkv.workspace_bytes
+    S, Hq, Hkv, D, B, L, Gn, Gs, P = 512, 40, 40, 128, 16, 1512, 64, 8, 992
+    n = sp(S, Hq, Hkv, D, B, L, Gn, Gs, P, 2)
+    vrows = Gn * Hq * Gs
+    want = (_up(vrows * D * 2) * 2 + _up(Gn * (P // B) * 4) + _up(Gn * 4) + _up(vrows * 4) + _up(S * Hq * 4)
+            + _up(ws(Gn, Hq * Gs, Hkv, D, B, P, 2)) + _up(ws(S, Hq, Hkv, D, B, L, 2)))
+    assert n == want
+    assert sp(S, Hq, Hkv, D, B, L, 0, 0, 0, 2) == _up(S * Hq * 4) + _up(ws(S, Hq, Hkv, D, B, L, 2))
+    assert sp(0, Hq, Hkv, D, B, L, Gn, Gs, P, 2) == 0
+    assert sp(S, Hq, Hkv, D, B, L, Gn, Gs, L + 1, 2) == 0                   # invalid -> 0
+
+
+def test_shared_prefix_checks_come_before_any_launch():
+    assert shared(k=ctypes.c_void_p(0x1004)) == -5
+    assert shared(scale=float("nan")) == -2
+    assert shared(N=0) == -2

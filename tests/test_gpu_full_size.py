@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import paged_kv_cache_339_amd as pkv
-from synthetic import CONFIGS, device_values, make_layout
+from synthetic import CONFIGS, device_values, make_layout, shared_prefix_groups
 from tests.gpu_util import (DeviceStep, assert_rows_close, ints, oracle_on_snapshot, say,
                             snapshot_sequences, to_storage_np, widen)
 
@@ -70,3 +70,16 @@ def test_full_size_sampled_rows(idx):
     got = widen(out.index_select(0, torch.tensor(seqs, device="cuda")))
     err = assert_rows_close(got, want, cfg.dtype, f"config {idx} full size")
     say(f"config {idx}: sampled sequences {seqs}, max row-relative error {err:.2e}")
+
+    if cfg.lengths == "shared_prefix":
+        # The call the benchmark times on this workload: each prompt's shared
+        # blocks read once for its samples (automatic partition, streamed).
+        members, prefix = shared_prefix_groups(lay)
+        out2 = torch.empty_like(step.q)
+        pkv.paged_attention_decode_shared_prefix(out2, step.q, step.k_cache, step.v_cache, step.tables, step.lens,
+                                                 ints(prefix), ints(members), int(prefix.max()), cfg.scale, B,
+                                                 cfg.num_kv_heads, lay.max_context_len)
+        torch.cuda.synchronize()
+        got2 = widen(out2.index_select(0, torch.tensor(seqs, device="cuda")))
+        err2 = assert_rows_close(got2, want, cfg.dtype, f"config {idx} full size, shared-prefix call")
+        say(f"config {idx}: shared-prefix call, max row-relative error {err2:.2e}")
