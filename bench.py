@@ -322,8 +322,11 @@ def beam_bench(args):
     """Beam search over the paged cache: each timed step is the host control
     plane (fork the chosen parents, free the old beams, reserve slots and
     copy-on-write pairs), the copies of tables / slots / pairs to the GPU,
-    pkv_copy_blocks and pkv_decode_step, then a stream synchronisation (a
-    real search reads the step's scores before choosing parents)."""
+    pkv_copy_blocks, pkv_reshape_and_cache and
+    pkv_paged_attention_decode_shared_prefix (each request's whole prompt
+    blocks read once for its beams; --per-sample-prefix: pkv_decode_step),
+    then a stream synchronisation (a real search reads the step's scores
+    before choosing parents)."""
     import torch
     import paged_kv_cache_339_amd as pkv
     from paged_kv_cache_339_amd._lib import CACHE_POLICIES, AttnOptions, lib
@@ -362,8 +365,15 @@ def beam_bench(args):
     M = -(-(cfg.prompt_len + cfg.steps + 1) // B)
     max_ctx = cfg.prompt_len + cfg.steps + 1
     code = dtype_code(kc)
-    ws = torch.empty(max(256, pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code)), dtype=torch.uint8,
-                     device=dev)
+    grouped = not args.per_sample_prefix
+    members_np, prefix_np = cache.shared_prefix()
+    members = torch.from_numpy(members_np).to(dev)
+    prefix_lens = torch.from_numpy(prefix_np).to(dev)
+    max_prefix = int(prefix_np.max())
+    ws_need = (pkv.shared_prefix_workspace_bytes(S, Hq, Hkv, D, B, max_ctx, R, Wb, max_prefix, code,
+                                                 cache_policy=policy) if grouped
+               else pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code))
+    ws = torch.empty(max(256, ws_need), dtype=torch.uint8, device=dev)
     out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
     pin = dict(tables=torch.empty((S, M), dtype=torch.int32).pin_memory(),
                lens=torch.empty(S, dtype=torch.int32).pin_memory(),
@@ -378,6 +388,7 @@ def beam_bench(args):
     step_start = [ev.create() for _ in range(total)]
     step_end = [ev.create() for _ in range(total)]
     kv_step = []
+    own_step = []       # bytes the timed kernel reads per step: K/V of its tokens and table entries
     host_s = []
 
     def step(t):
@@ -399,15 +410,31 @@ def beam_bench(args):
                                      Hkv, B, D, N, code, vp(stream.cuda_stream))
             assert st == 0, st
         opts = AttnOptions(0, 0, begins[t], ends[t], 0, 0, 1.0, 1.0, 0, CACHE_POLICIES[policy])
-        st = lib.pkv_decode_step(vp(out.data_ptr()), vp(qs[t].data_ptr()), vp(ks[t].data_ptr()), vp(vs[t].data_ptr()),
-                                 vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["slots"].data_ptr()),
-                                 vp(dbuf["tables"].data_ptr()), vp(dbuf["lens"].data_ptr()), cfg.scale, B, Hkv, S,
-                                 Hq, D, M, max_ctx, N, code, vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
-                                 vp(stream.cuda_stream))
-        assert st == 0, st
+        if grouped:
+            st = lib.pkv_reshape_and_cache(vp(ks[t].data_ptr()), vp(vs[t].data_ptr()), vp(kc.data_ptr()),
+                                           vp(vc.data_ptr()), vp(dbuf["slots"].data_ptr()), S, Hkv, D, B, N, code,
+                                           vp(stream.cuda_stream))
+            assert st == 0, st
+            st = lib.pkv_paged_attention_decode_shared_prefix(
+                vp(out.data_ptr()), vp(qs[t].data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                vp(dbuf["tables"].data_ptr()), vp(dbuf["lens"].data_ptr()), vp(prefix_lens.data_ptr()),
+                vp(members.data_ptr()), R, Wb, max_prefix, cfg.scale, B, Hkv, S, Hq, D, M, max_ctx, N, code,
+                vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream.cuda_stream))
+            assert st == 0, st
+        else:
+            st = lib.pkv_decode_step(vp(out.data_ptr()), vp(qs[t].data_ptr()), vp(ks[t].data_ptr()),
+                                     vp(vs[t].data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()),
+                                     vp(dbuf["slots"].data_ptr()), vp(dbuf["tables"].data_ptr()),
+                                     vp(dbuf["lens"].data_ptr()), cfg.scale, B, Hkv, S, Hq, D, M, max_ctx, N, code,
+                                     vp(ws.data_ptr()), ws.numel(), ctypes.byref(opts), vp(stream.cuda_stream))
+            assert st == 0, st
         ev.record(step_end[t], stream.cuda_stream)
         stream.synchronize()
         kv_step.append(kv_bytes(lens, Hkv, D, cfg.dtype))
+        l64 = lens.astype(np.int64)
+        own = l64 - (prefix_np if grouped else 0)
+        own_blk = -(-l64 // B) - ((prefix_np // B) if grouped else 0)
+        own_step.append(int(own.sum()) * Hkv * D * 2 * es + int(own_blk.sum()) * 4 * Hkv)
 
     for t in range(W):
         step(t)
@@ -424,16 +451,19 @@ def beam_bench(args):
     kv = float(np.mean(kv_step[W:]))
     step_s = wall / K
     main_s = float(np.mean(main_ms)) / 1e3
-    alg = kv + 2 * S * Hq * D * es + S * M * 4 * Hkv + S * 4
+    alg = float(np.mean(own_step[W:])) + 2 * S * Hq * D * es + S * (8 if grouped else 4)
+    tag = cfg.name + ("" if policy == base.cache_policy else f"_{policy}") + ("" if grouped else "_persample")
     print(json.dumps({
         "metric": METRIC, "value": round(kv / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": cfg.name + ("" if policy == base.cache_policy else f"_{policy}"),
+        "config": {"workload": tag,
                    "cache_policy": policy, "requests": R, "beam_width": Wb, "prompt_len": cfg.prompt_len,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B, "kv_dtype": cfg.dtype,
                    "pool_blocks": N, "kv_bytes_per_step": int(kv),
-                   "step": "host fork/free/append + H2D tables + copy_blocks + decode_step + sync"},
+                   "step": "host fork/free/append + H2D tables + copy_blocks + " + (
+                       "reshape_and_cache + decode_shared_prefix (each request's prompt blocks read once) + sync"
+                       if grouped else "decode_step + sync")},
         "pct_hbm_peak": round(100 * kv / step_s / 1e9 / HBM_PEAK_GBPS, 2),
         "seq_heads_per_s": round(S * Hq / step_s, 1),
         "host_ms_per_step": round(1e3 * float(np.mean(host_s[W:])), 4),
@@ -441,7 +471,9 @@ def beam_bench(args):
         "roofline": {"bound": "hbm", "achieved": round(alg / main_s / 1e9, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(alg / main_s / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "attn_valu_kernel", "bytes_per_launch": int(alg),
-                     "note": "logical bytes: the beams of a request share their prompt blocks, served from cache"},
+                     "note": ("the pass over each beam's own tokens (the prompt's whole blocks are read by the "
+                              "grouped pass)") if grouped else
+                             "logical bytes: the beams of a request share their prompt blocks, served from cache"},
         "cpu_baseline": cpu,
     }), flush=True)
 

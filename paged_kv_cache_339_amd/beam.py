@@ -9,7 +9,9 @@ beams are released, and one token is appended to every new beam, which
 copies a shared last block first ("Copy-on-Write Sharing > Divergence
 Handling").  Everything here runs on the host through the library's C++
 block manager; the copies, token stores and attention are the caller's
-pkv_copy_blocks and pkv_decode_step calls with the arrays returned.
+pkv_copy_blocks and pkv_decode_step calls with the arrays returned (or
+pkv_paged_attention_decode_shared_prefix with shared_prefix(), which reads
+each request's prompt blocks once for all its beams).
 
 Sequence ids alternate between two banks of R*W ids so that a step's new
 beams never collide with the old ones they fork from.
@@ -28,6 +30,7 @@ class BeamSearchCache:
         self.bm = BlockManager(num_blocks, block_size, 2 * num_requests * beam_width, free_order)
         self.bank = 0
         self.started = False
+        self.prompt_len = 0
 
     def seq_ids(self, bank=None) -> np.ndarray:
         """Ids of the live beams, request-major: [R * W]."""
@@ -38,6 +41,7 @@ class BeamSearchCache:
     def prefill(self, prompt_len: int) -> np.ndarray:
         """Beam 0 of every request takes the prompt.  Returns the slots of the
         prompt tokens, [R, prompt_len] (request r's keys and values go there)."""
+        self.prompt_len = prompt_len
         ids = self.seq_ids()
         slots = np.zeros((self.R, prompt_len), dtype=np.int32)
         for r in range(self.R):
@@ -64,6 +68,17 @@ class BeamSearchCache:
         self.bank = 1 - self.bank
         slots, pairs = self.bm.append_batch(new)
         return new, slots, pairs
+
+    def shared_prefix(self):
+        """Groups for pkv_paged_attention_decode_shared_prefix over the rows of
+        tables(): the beams of each request [R, W] (rows, request-major), and
+        for every beam the prompt tokens held in whole blocks.  Every beam
+        descends from its request's prompt, so those blocks stay shared by all
+        W beams; a partial last prompt block is copied on divergence and is
+        read with each beam's own tokens."""
+        members = np.arange(self.R * self.W, dtype=np.int32).reshape(self.R, self.W)
+        prefix = np.full(self.R * self.W, self.prompt_len // self.B * self.B, dtype=np.int32)
+        return members, prefix
 
     def tables(self, max_blocks: int):
         """Block tables [R*W, max_blocks] (-1 padded) and lengths of the live beams."""

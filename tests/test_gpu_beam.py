@@ -83,6 +83,14 @@ def test_beam_search_steps_match_the_oracle(R, W, P, steps, B, dtype, Hq, Hkv):
         oracle.reshape_and_cache(kn, vn, host_k, host_v, slots, B)
         want = oracle.paged_attention_decode(q, host_k, host_v, tables, lens, cfg.scale, B, Hkv, dtype)
         assert_rows_close(widen(out), want, dtype, f"beam step {t}")
+        # The same attention with each request's prompt blocks read once for its beams.
+        members, prefix = cache.shared_prefix()
+        out2 = torch.empty_like(out)
+        pkv.paged_attention_decode_shared_prefix(out2, to_device(q, dtype), dev_k, dev_v, ints(tables), ints(lens),
+                                                 ints(prefix), ints(members), int(prefix.max()), cfg.scale, B,
+                                                 Hkv, int(lens.max()))
+        torch.cuda.synchronize()
+        assert_rows_close(widen(out2), want, dtype, f"beam step {t}, shared-prefix call")
     assert to_storage_np(dev_k, dtype).tobytes() == host_k.tobytes(), "key pool differs after the search"
     assert to_storage_np(dev_v, dtype).tobytes() == host_v.tobytes(), "value pool differs after the search"
     cache.close()
