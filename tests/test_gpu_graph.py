@@ -81,3 +81,59 @@ def test_captured_multi_layer_step_replays_bit_identically(idx, scaled):
         # Eager work between replays on the same tensors and workspace.
         run(eager)
         torch.cuda.synchronize()
+
+
+def test_captured_shared_prefix_layers_replay_bit_identically():
+    """The shared-prefix call (prep, grouped pass, own-token pass, merge) in a
+    captured multi-layer step: the first layer builds both work lists, the
+    others reuse them."""
+    from synthetic import shared_prefix_groups
+    from tests.gpu_util import ints
+    cfg = CONFIGS[5].scaled(num_seqs=12, num_q_heads=8, num_kv_heads=8, samples_per_prompt=4, prompt_len=150,
+                            len_hi=60, partition_size=0, cache_policy="stream")
+    lay = make_layout(cfg, seed=95)
+    base = DeviceStep.from_host(lay, host_values(lay))
+    base.scatter()
+    members, prefix = shared_prefix_groups(lay)
+    mem, pre = ints(members), ints(prefix)
+    S, layers, max_ctx = len(lay.context_lens), 3, lay.max_context_len
+    say(f"graph capture, shared prefix S={S} layers={layers}")
+    code = pkv.ops.dtype_code(base.q)
+    ws = torch.empty(pkv.shared_prefix_workspace_bytes(S, 8, 8, cfg.head_dim, cfg.block_size, max_ctx,
+                                                       members.shape[0], members.shape[1], int(prefix.max()), code),
+                     dtype=torch.uint8, device="cuda")
+
+    def layer_data(l):
+        f = _sign_flipped if l % 2 else (lambda t: t)
+        return dict(q=f(base.q).clone(), kc=f(base.k_cache).clone(), vc=f(base.v_cache).clone(),
+                    out=torch.empty_like(base.q))
+
+    def run(data):
+        for l, d in enumerate(data):
+            pkv.paged_attention_decode_shared_prefix(d["out"], d["q"], d["kc"], d["vc"], base.tables, base.lens,
+                                                     pre, mem, int(prefix.max()), cfg.scale, cfg.block_size,
+                                                     cfg.num_kv_heads, max_ctx, workspace=ws, reuse_plan=l > 0)
+
+    eager = [layer_data(l) for l in range(layers)]
+    run(eager)
+    torch.cuda.synchronize()
+    graph_data = [layer_data(l) for l in range(layers)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(graph_data)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(graph_data)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        for d in graph_data:
+            d["out"].zero_()
+        run(eager)                       # eager work between the replays, on the same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (d, e) in enumerate(zip(graph_data, eager)):
+            assert torch.equal(d["out"].view(torch.int16), e["out"].view(torch.int16)), (replay, l)
