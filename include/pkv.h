@@ -286,7 +286,8 @@ int pkv_decode_step(void* out, const void* q, const void* k_new, const void* v_n
  * NaN as in pkv_paged_attention_decode.
  * opts: as pkv_paged_attention_decode, except sliding_window (must be 0:
  * PKV_ERR_UNSUPPORTED) and kernel and the events, which apply to the
- * whole-batch pass only.  workspace: at least
+ * whole-batch pass only; the grouped pass rounds partition_size up to a
+ * multiple of 32 tokens (and of block_size) when it is not one.  workspace: at least
  * pkv_paged_attention_shared_prefix_workspace_bytes bytes, 16-byte aligned.
  * num_groups = 0 is a plain decode.
  */

@@ -437,6 +437,10 @@ int prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, i
   L->suf = o;
   L->pre = o;
   L->pre.kernel = PKV_KERNEL_AUTO;       // the virtual batch is grouped-query
+  // A partition size valid for the whole-batch pass may not suit the matrix
+  // cores (whole 32-token chunks): the grouped pass rounds it up.
+  if (o.partition_size > 0)
+    L->pre.partition_size = (int32_t)round_up((size_t)o.partition_size, block_size > 32 ? block_size : 32);
   L->pre.main_begin_event = L->pre.main_end_event = nullptr;
   Plan suf, pre;
   int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,

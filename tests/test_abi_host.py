@@ -309,3 +309,13 @@ def test_shared_prefix_checks_come_before_any_launch():
     assert shared(k=ctypes.c_void_p(0x1004)) == -5
     assert shared(scale=float("nan")) == -2
     assert shared(N=0) == -2
+
+
+def test_shared_prefix_partition_suits_both_passes():
+    # 16-token partitions suit the vector kernel of the whole batch; the
+    # grouped pass (matrix cores, 8 heads per KV head) rounds them up to 32
+    # instead of refusing the call: it gets as far as the workspace check.
+    opts = AttnOptions(16, 0, None, None)
+    assert shared(dtype=2, Hq=2, Hkv=2, Gs=8, opts=ctypes.byref(opts)) == -6
+    bad = AttnOptions(24, 0, None, None)                     # not a multiple of the block size
+    assert shared(dtype=2, opts=ctypes.byref(bad)) == -2

@@ -61,7 +61,7 @@ def test_shared_prefix_every_row(dtype, Hq, Hkv, B):
     assert_rows_close(got, plain, dtype, "shared-prefix decode vs plain decode")
 
 
-@pytest.mark.parametrize("partition_size", [32, 64, 512])
+@pytest.mark.parametrize("partition_size", [16, 32, 64, 512])
 def test_shared_prefix_with_split_partitions(partition_size):
     cfg = scaled("bf16", 8, 8, prompt_len=700, tail=300)
     lay = make_layout(cfg, seed=52)
