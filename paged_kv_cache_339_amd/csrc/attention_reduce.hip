@@ -11,8 +11,8 @@ namespace pkv {
 
 // One workgroup per (sequence, head chunk): the chunk's rows of a partition
 // are one contiguous run, read 8 elements (one 16-byte load of a 16-bit
-// row) per lane.  kReduceSplit groups of lanes take the partitions in turn
-// (group k: partitions k, k + kReduceSplit, ...), so the longest sequences
+// row) per lane.  Up to kReduceSplit groups of lanes take the partitions in
+// turn (group k of n: partitions k, k + n, ...), so the longest sequences
 // wait on a quarter of the dependent load rounds.  Each group merges its
 // partitions in order, as online softmax:
 // M' = max(M, m_p), W = W 2^(M - M') + l_p 2^(m_p - M'), and O likewise with
@@ -55,7 +55,7 @@ __device__ __forceinline__ void merge_state(MergeState& st, const MergeState& o)
 template <int DT, int D>
 __global__ __launch_bounds__(kReduceLanes * kReduceSplit) void attn_reduce_kernel(AttnParams p, int B) {
   constexpr int E = kReduceElems;
-  __shared__ MergeState lds[kReduceSplit - 1][kReduceLanes];
+  extern __shared__ MergeState lds[];      // [split - 1][per]
   const int slots = p.num_kv_heads * p.chunks;
   const int s = blockIdx.x / slots;
   const int slot = blockIdx.x - s * slots;
@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kReduceLanes * kReduceSplit) void attn_reduce_kerne
   if (sw.bad || sw.nparts <= 1) return;     // written by the main kernel (workgroup-uniform)
   const int G = p.cap;                      // rows per run in the workspace
   const size_t run0 = ((size_t)s * slots + slot) * p.max_parts;   // partition 0's first row is run0 * G
-  const int per = blockDim.x / kReduceSplit;                       // lanes per group
+  const int split = min(kReduceSplit, p.max_parts);                // groups of lanes
+  const int per = blockDim.x / split;                              // lanes per group
   const int grp = threadIdx.x / per, lt = threadIdx.x - grp * per;
   // Every lane runs the same number of rounds (barriers inside).
   for (int e0 = 0; e0 < rows * D; e0 += per * E) {
@@ -79,11 +80,11 @@ __global__ __launch_bounds__(kReduceLanes * kReduceSplit) void attn_reduce_kerne
 #pragma unroll
     for (int k = 0; k < E; ++k) st.O[k] = 0.f;
     if (live) {
-      for (int i0 = grp; i0 < sw.nparts; i0 += kReduceSplit * kReduceAhead) {
+      for (int i0 = grp; i0 < sw.nparts; i0 += split * kReduceAhead) {
         float m[kReduceAhead], l[kReduceAhead], o[kReduceAhead][E];
 #pragma unroll
         for (int k = 0; k < kReduceAhead; ++k) {
-          const int i = min(i0 + k * kReduceSplit, sw.nparts - 1);
+          const int i = min(i0 + k * split, sw.nparts - 1);
           const size_t row = (run0 + i) * G + g;
           const f32x2v ml = *reinterpret_cast<const f32x2v*>(p.ws_ml + row * 2);
           m[k] = ml[0];
@@ -92,16 +93,16 @@ __global__ __launch_bounds__(kReduceLanes * kReduceSplit) void attn_reduce_kerne
         }
 #pragma unroll
         for (int k = 0; k < kReduceAhead; ++k) {
-          if (i0 + k * kReduceSplit >= sw.nparts) break;
+          if (i0 + k * split >= sw.nparts) break;
           merge_into(st, m[k], l[k], o[k]);
         }
       }
     }
-    if (grp > 0) lds[grp - 1][lt] = st;
+    if (grp > 0) lds[(grp - 1) * per + lt] = st;
     __syncthreads();
     if (grp == 0 && live) {
 #pragma unroll
-      for (int k = 0; k < kReduceSplit - 1; ++k) merge_state(st, lds[k][lt]);
+      for (int k = 0; k < split - 1; ++k) merge_state(st, lds[k * per + lt]);
       float r[E];
 #pragma unroll
       for (int j = 0; j < E; ++j) r[j] = st.O[j] / st.W;
@@ -116,10 +117,15 @@ namespace {
 template <int DT, int D>
 hipError_t launch_reduce(const AttnParams& p, int B, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.chunks));
-  // Lanes take 8 elements each; small groups need fewer lanes.
-  const int rows = p.chunk_rows * D / kReduceElems;
-  const int per = min(kReduceLanes, max(kWave, (rows + kWave - 1) / kWave * kWave));
-  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(per * kReduceSplit), 0, st, p, B);
+  // Lanes take 8 elements each: a group has the row's lanes rounded up to a
+  // power of two (16 to 256), and a sequence of P partitions needs at most
+  // P groups.
+  const int lanes = p.chunk_rows * D / kReduceElems;
+  int per = 16;
+  while (per < lanes && per < kReduceLanes) per *= 2;
+  const int split = min(kReduceSplit, p.max_parts);
+  const size_t lds = (size_t)(split - 1) * per * sizeof(MergeState);
+  hipLaunchKernelGGL((attn_reduce_kernel<DT, D>), grid, dim3(per * split), lds, st, p, B);
   return hipGetLastError();
 }
 
