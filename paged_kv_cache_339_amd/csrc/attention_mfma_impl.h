@@ -145,6 +145,10 @@ template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 4> {
 #define PKV_MFMA_OCC 2
 #endif
 
+// How far (log2 units) a score may pass a head's running reference before
+// the reference is raised to the exact maximum.
+constexpr float kRefSlack = 16.f;
+
 // NT: key/value loads with the nontemporal hint (see load_kv).
 template <int DT, int KT, int D, int B, int G, int NW, int U, bool NT>
 __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(AttnParams p) {
@@ -323,15 +327,27 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
             if (c0 + 8 * q + j >= L || c0 + 8 * q + j < t0) sc[j] = -INFINITY;
         }
 
+        // The running reference m of a head need not be its exact maximum,
+        // only shared by the head's lanes and not exceeded by more than
+        // kRefSlack (weights up to 2^kRefSlack, finite in fp32 and in the
+        // 16-bit operands).  So the cross-lane maximum (two ds_bpermute
+        // round trips on the chunk's critical path) is taken only when some
+        // score passes that bound, or while m is still -inf.
         float cm = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
-        cm = fmaxf(cm, shfl_xor_f(cm, 16));
-        cm = fmaxf(cm, shfl_xor_f(cm, 32));
-        const float mn = fmaxf(m[ct], cm);
-        const float ref = softmax_ref(mn);
-        alpha[ct] = fast_exp2(m[ct] - ref);
-        m[ct] = mn;
+        float ref;
+        if (__any(cm > m[ct] + kRefSlack || m[ct] == -INFINITY)) {
+          cm = fmaxf(cm, shfl_xor_f(cm, 16));
+          cm = fmaxf(cm, shfl_xor_f(cm, 32));
+          const float mn = fmaxf(m[ct], cm);
+          ref = softmax_ref(mn);
+          alpha[ct] = fast_exp2(m[ct] - ref);
+          m[ct] = mn;
+        } else {
+          ref = m[ct];
+          alpha[ct] = 1.f;
+        }
 
         // Weights rounded to the operand format; the sum adds the rounded
         // values (in fp32, on the matrix core).

@@ -253,6 +253,9 @@ WINDOW_CASES = [
     # dtype, B, Hq, Hkv, kernel
     ("bf16", 16, 32, 8, "mfma"), ("bf16", 16, 32, 8, "valu"), ("f16", 32, 8, 8, "valu"),
     ("f32", 16, 2, 1, "valu"), ("f16", 8, 16, 1, "mfma"),
+    # 64-token blocks on the matrix cores: the first 32-token chunk can lie
+    # wholly before the window's first token (every score masked).
+    ("bf16", 64, 16, 2, "mfma"),
 ]
 
 
