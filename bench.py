@@ -789,7 +789,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # The arithmetic the main kernel computes in: fp32 on the vector ALUs;
+        # 16-bit operands (8-bit codes widened to them) with fp32 accumulation
+        # on the matrix cores.
+        "dtype": "f32" if kernel_used == "valu" else cfg.dtype,
         "data": "synthetic",
         "config": {
             "workload": tag,
