@@ -146,8 +146,9 @@ template <int DT> struct VLoad<DT, PKV_FP8_E4M3, 4> {
 #endif
 
 // How far (log2 units) a score may pass a head's running reference before
-// the reference is raised to the exact maximum.
-constexpr float kRefSlack = 16.f;
+// the reference is raised to the exact maximum: weights stay below
+// 2^kRefSlack = 256, far inside the fp16 operand range (65504).
+constexpr float kRefSlack = 8.f;
 
 // NT: key/value loads with the nontemporal hint (see load_kv).
 template <int DT, int KT, int D, int B, int G, int NW, int U, bool NT>
@@ -329,8 +330,8 @@ __global__ __launch_bounds__(NW * kWave, PKV_MFMA_OCC) void attn_mfma_kernel(Att
 
         // The running reference m of a head need not be its exact maximum,
         // only shared by the head's lanes and not exceeded by more than
-        // kRefSlack (weights up to 2^kRefSlack, finite in fp32 and in the
-        // 16-bit operands).  So the cross-lane maximum (two ds_bpermute
+        // kRefSlack (weights up to 2^kRefSlack, exact enough and finite in
+        // fp32 and in either 16-bit operand format).  So the cross-lane maximum (two ds_bpermute
         // round trips on the chunk's critical path) is taken only when some
         // score passes that bound, or while m is still -inf.
         float cm = sc[0];

@@ -455,3 +455,31 @@ def test_cache_policies_give_identical_bits(idx):
         b = step.attend(partition_size=part, cache_policy="keep").clone()
         torch.cuda.synchronize()
         assert torch.equal(a.view(view), b.view(view)), part
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_score_jumps_around_the_running_reference(dtype, partition_size):
+    """The matrix-core kernel keeps a head's softmax reference until a score
+    passes it by more than a factor 2^8.  Scores that jump by 7.9 to 24 (log2
+    units) over the running maximum, chunk after chunk, must neither overflow
+    the 16-bit weights nor lose accuracy: checked against the oracle."""
+    rng = np.random.default_rng(77)
+    Hq, Hkv, D, B, L = 8, 1, 128, 32, 256
+    scale = 1.0 / np.sqrt(D)
+    q = rng.standard_normal((1, Hq, D))
+    K = 0.05 * rng.standard_normal((L, Hkv, D))
+    V = rng.standard_normal((L, Hkv, D))
+    import oracle
+    q0 = pins.widen(pins.to_storage(q[0, 0], dtype), dtype)
+    unit = scale * np.log2(np.e) * float(q0 @ q0)         # log2-units score of k = q0
+    level = 0.0
+    for t, jump in zip(range(40, L, 29), [7.9, 8.1, 12.0, 15.95, 16.0, 16.05, 24.0, 3.0]):
+        level += jump
+        K[t, 0] = q0 * (level / unit)
+    qs = pins.to_storage(q, dtype)
+    p = pins.Paged([pins.to_storage(K, dtype)], [pins.to_storage(V, dtype)], qs, B, dtype, 5)
+    say(f"score jumps {dtype} partition {partition_size}")
+    got = _paged_on_gpu(p, dtype, scale, Hkv, kernel="mfma", partition_size=partition_size)
+    want = p.run(oracle.paged_attention_decode, scale, Hkv)
+    assert_rows_close(widen(got), want, dtype, f"score jumps ({dtype}, partition {partition_size})")
