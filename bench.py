@@ -375,11 +375,20 @@ def beam_bench(args):
                else pkv.workspace_bytes(S, Hq, Hkv, D, B, max_ctx, code))
     ws = torch.empty(max(256, ws_need), dtype=torch.uint8, device=dev)
     out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
-    pin = dict(tables=torch.empty((S, M), dtype=torch.int32).pin_memory(),
-               lens=torch.empty(S, dtype=torch.int32).pin_memory(),
-               slots=torch.empty(S, dtype=torch.int32).pin_memory(),
-               pairs=torch.empty((S, 2), dtype=torch.int32).pin_memory())
-    dbuf = {k: torch.empty(v.shape, dtype=torch.int32, device=dev) for k, v in pin.items()}
+    # The step's tables, lengths, slots and copy pairs travel in one pinned
+    # buffer and one copy (each piece starting on 16 bytes).
+    shapes = dict(tables=(S, M), lens=(S,), slots=(S,), pairs=(S, 2))
+    offs, total_ints = {}, 0
+    for k, shp in shapes.items():
+        offs[k] = total_ints
+        total_ints += -(-int(np.prod(shp)) // 4) * 4
+    host_flat = torch.empty(total_ints, dtype=torch.int32).pin_memory()
+    dev_flat = torch.empty(total_ints, dtype=torch.int32, device=dev)
+
+    def views(flat):
+        return {k: flat[offs[k]:offs[k] + int(np.prod(shp))].view(shp) for k, shp in shapes.items()}
+
+    pin, dbuf = views(host_flat), views(dev_flat)
     stream = torch.cuda.current_stream()
     ev = HipEvents()
     vp = ctypes.c_void_p
@@ -403,8 +412,7 @@ def beam_bench(args):
         if n_pairs:
             pin["pairs"].numpy()[:n_pairs] = pairs
         ev.record(step_start[t], stream.cuda_stream)
-        for k in dbuf:
-            dbuf[k].copy_(pin[k], non_blocking=True)
+        dev_flat.copy_(host_flat, non_blocking=True)
         if n_pairs:
             st = lib.pkv_copy_blocks(vp(kc.data_ptr()), vp(vc.data_ptr()), vp(dbuf["pairs"].data_ptr()), n_pairs,
                                      Hkv, B, D, N, code, vp(stream.cuda_stream))
