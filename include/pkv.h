@@ -209,7 +209,9 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * and the grid ends on short ones), then the main kernel, one workgroup per
  * (pair, KV head, head chunk); and, when a sequence can span several partitions, the
  * split-K reduce, which merges the partial softmax states in partition
- * order.  The schedule does not change any result.
+ * order.  A main grid of at most 256 workgroups is resident at once: it
+ * takes its items in grid order and no plan kernel runs.  The schedule
+ * does not change any result.
  * Data errors are contained, never dereferenced: a table entry outside
  * [0, num_blocks), or context_lens[s] above max_context_len or
  * max_blocks_per_seq * B, makes that sequence's output rows NaN.

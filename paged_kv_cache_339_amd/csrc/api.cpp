@@ -33,6 +33,9 @@ constexpr int64_t kMaxGrid = 0xffffffffll / 256;
 constexpr int64_t kNoSplitPairs = 2048;
 constexpr int64_t kFillItems = 4096;
 constexpr int64_t kMinAutoPartition = 1024;
+// A grid of at most this many workgroups (one per compute unit) is resident
+// at once: the order of its items does not matter, so no work list is built.
+constexpr int64_t kDirectGrid = 256;
 
 int dtype_bytes(pkv_dtype dt) {
   switch (dt) {
@@ -55,6 +58,7 @@ struct Plan {
   int kernel;
   bool fp8;
   bool keep;          // plain key/value loads (PKV_CACHE_KEEP, or head chunks)
+  bool direct;        // small grid: items taken in grid order, no work list
   int32_t chunks;     // workgroups per (sequence, KV head, partition)
   int32_t chunk_rows; // query heads per chunk (the last may have fewer)
   int32_t cap;        // instance's query heads per workgroup, >= chunk_rows
@@ -167,6 +171,7 @@ int make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32
   const int64_t grid = plan->chunks > 1 ? (items + 7) / 8 * 8 * plan->chunks : items;
   if (grid > kMaxGrid) return PKV_ERR_SHAPE;
   plan->kernel = kernel;
+  plan->direct = grid <= kDirectGrid;
   plan->max_pairs = (int64_t)num_seqs * plan->max_parts;
   plan->pairs_off = round_up(sizeof(pkv::WorkHeader), 256);
   plan->ws_o_off = plan->pairs_off + round_up((size_t)plan->max_pairs * sizeof(pkv::WorkPair), 256);
@@ -316,15 +321,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.items = (int32_t)((int64_t)num_seqs * num_kv_heads * plan.max_parts);
   p.seq_start = seq_start;
   p.lse = lse;
+  p.direct = plan.direct ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_pending_error();
   const bool reuse = opts && opts->reuse_plan;
   hipError_t err = hipSuccess;
   if (append) {
-    append->plan = reuse ? 0 : 1;
+    append->plan = (reuse || plan.direct) ? 0 : 1;
     err = pkv::launch_append_and_plan(p, block_size, *append, s);
-  } else if (!reuse) {
+  } else if (!reuse && !plan.direct) {
     err = pkv::launch_attention_plan(p, block_size, s);
   }
   if (err != hipSuccess) return launch_status(err);

@@ -78,15 +78,21 @@ __device__ __forceinline__ WorkItem work_item(const AttnParams& p) {
   const int pair = in_grid ? u / p.num_kv_heads : 0;
   WorkItem it;
   it.h = u - pair * p.num_kv_heads;
+  it.slot = it.h * p.chunks + c;
+  it.q0 = it.h * p.group + c * p.chunk_rows;
+  it.rows = min(p.chunk_rows, p.group - c * p.chunk_rows);
+  if (p.direct) {
+    it.s = pair / p.max_parts;
+    it.part = pair - it.s * p.max_parts;
+    it.valid = in_grid && it.s < p.num_seqs && it.rows > 0;
+    return it;
+  }
   // The pair is loaded before the list length so that both loads are in
   // flight together (the other order made the compiler wait in between).
   const WorkPair wp = p.pairs[pair];
   const int n_pairs = min(p.work->n_pairs, p.max_pairs);
   it.s = wp.s;
   it.part = wp.part;
-  it.slot = it.h * p.chunks + c;
-  it.q0 = it.h * p.group + c * p.chunk_rows;
-  it.rows = min(p.chunk_rows, p.group - c * p.chunk_rows);
   it.valid = in_grid && pair < n_pairs && (unsigned)wp.s < (unsigned)p.num_seqs &&
              (unsigned)wp.part < (unsigned)p.max_parts && it.rows > 0;
   return it;

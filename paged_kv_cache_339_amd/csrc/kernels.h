@@ -59,6 +59,11 @@ struct AttnParams {
   // scale_log2: log2 sum_t 2^(scale_log2 <q, k_t>) (-inf for an empty row).
   const int32_t* seq_start;
   float* lse;
+  // Nonzero: the grid is small enough to be resident at once, so the order
+  // of the work items does not matter; workgroup u takes pair u / Hkv as
+  // (sequence, partition) = (pair / max_parts, pair % max_parts) and no
+  // work list is built or read.
+  int32_t direct;
 };
 
 // Workgroups of a main-kernel launch: one per work item and head chunk;
