@@ -238,7 +238,12 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
  * by the same launch that builds the attention work list, then attention
  * runs as pkv_paged_attention_decode over context_lens (which count the new
  * token).  Results are bit-identical to those two calls in sequence; the
- * step saves one launch.  With opts->reuse_plan the first launch only
+ * step saves one launch.  slot_mapping[i] must be the slot of token L_i - 1
+ * of sequence i's table (as the block manager hands it out): a small batch
+ * on the vector kernel with caches in the query format runs the whole step
+ * in one launch, whose attention takes that token's key and value from
+ * k_new and v_new rather than from the cache (a slot outside the pool is
+ * neither stored nor substituted).  With opts->reuse_plan the first launch only
  * stores the tokens.  With an 8-bit cache format the tokens are stored as
  * pkv_reshape_and_cache_fp8 would, with the options' scales.  k_new, v_new:
  * device [num_seqs, num_kv_heads, head_dim] in the query format, 16-byte

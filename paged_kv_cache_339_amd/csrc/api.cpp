@@ -322,15 +322,24 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.seq_start = seq_start;
   p.lse = lse;
   p.direct = plan.direct ? 1 : 0;
+  // A small-grid decode step on the vector kernel (caches in the query
+  // format) runs in one launch: the attention workgroups store the new
+  // tokens and read them from the inputs.
+  const bool fuse = append != nullptr && plan.direct && plan.kernel == PKV_KERNEL_VALU && !plan.fp8 &&
+                    !append->fp8;
+  p.new_k = fuse ? append->k : nullptr;
+  p.new_v = fuse ? append->v : nullptr;
+  p.new_slots = fuse ? append->slot_mapping : nullptr;
+  p.num_slots = fuse ? append->num_slots : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_pending_error();
   const bool reuse = opts && opts->reuse_plan;
   hipError_t err = hipSuccess;
-  if (append) {
+  if (append && !fuse) {
     append->plan = (reuse || plan.direct) ? 0 : 1;
     err = pkv::launch_append_and_plan(p, block_size, *append, s);
-  } else if (!reuse && !plan.direct) {
+  } else if (!append && !reuse && !plan.direct) {
     err = pkv::launch_attention_plan(p, block_size, s);
   }
   if (err != hipSuccess) return launch_status(err);

@@ -41,6 +41,25 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   const int grp = lane / LPT, sub = lane % LPT;
   const int Hkv = p.num_kv_heads;
 
+  // Decode step in one launch: the appended token's key and value rows go to
+  // their slot (one workgroup per sequence and KV head, whatever its length),
+  // and the attention below takes them from the inputs, not the cache.
+  // A token without a slot (outside [0, num_slots)) is neither stored nor
+  // substituted: attention then reads the cache, as after a separate store.
+  constexpr int kRowPieces = D * ES / 16;
+  bool fused = false;
+  if (p.new_k != nullptr) {
+    const int32_t slot = p.new_slots[it.s];
+    fused = slot >= 0 && (int64_t)slot < p.num_slots;
+    if (fused && it.part == 0 && it.q0 == it.h * p.group && threadIdx.x < kRowPieces) {
+      const size_t src = (((size_t)it.s * Hkv + it.h) * kRowPieces + threadIdx.x) * 16;
+      const u32x4 a = load16(p.new_k + src), b = load16(p.new_v + src);
+      const size_t dst = ((((size_t)(slot / B) * Hkv + it.h) * B + slot % B) * kRowPieces + threadIdx.x) * 16;
+      store16(reinterpret_cast<char*>(const_cast<void*>(p.k_cache)) + dst, a);
+      store16(reinterpret_cast<char*>(const_cast<void*>(p.v_cache)) + dst, b);
+    }
+  }
+
   // The first 64 table entries of the partition are fetched before the
   // sequence length is known (they lie inside the row whatever the length),
   // one per lane, so translating a block later is a register read.
@@ -121,14 +140,24 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
         const size_t lane_off = (((size_t)(ok ? phys : 0) * Hkv + it.h) * B + grp) * D + sub * EPL;
         const char* kt = kbase + lane_off * ES;
         const char* vt = vbase + lane_off * ES;
+        // Row tail - 1 of the last block is token L - 1: in a one-launch
+        // decode step it comes from the step's inputs.
+        const int new_row = (fused && c0 + jj == last) ? tail - 1 : -1;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           kr[u][i] = u32x4{0, 0, 0, 0};
           vr[u][i] = u32x4{0, 0, 0, 0};
           const int row = i * TPW + grp;
           if (row >= first[u] && row < valid[u]) {
-            kr[u][i] = load_kv<NT, u32x4>(kt + (size_t)i * TPW * D * ES);
-            vr[u][i] = load_kv<NT, u32x4>(vt + (size_t)i * TPW * D * ES);
+            const char* kp = kt + (size_t)i * TPW * D * ES;
+            const char* vp = vt + (size_t)i * TPW * D * ES;
+            if (row == new_row) {
+              const size_t nr = (((size_t)it.s * Hkv + it.h) * D + sub * EPL) * ES;
+              kp = p.new_k + nr;
+              vp = p.new_v + nr;
+            }
+            kr[u][i] = load_kv<NT, u32x4>(kp);
+            vr[u][i] = load_kv<NT, u32x4>(vp);
           }
         }
       }

@@ -64,6 +64,15 @@ struct AttnParams {
   // (sequence, partition) = (pair / max_parts, pair % max_parts) and no
   // work list is built or read.
   int32_t direct;
+  // Optional (new_k = nullptr: none), for a small-grid decode step on the
+  // vector kernel with caches in the query format: the step's new tokens
+  // [S, Hkv, D], stored by the workgroup of (sequence, KV head, partition 0,
+  // chunk 0) at new_slots[s] (skipped outside [0, num_slots)), and read
+  // from here instead of the cache as token L - 1 of their sequence.
+  const char* new_k;
+  const char* new_v;
+  const int32_t* new_slots;
+  int64_t num_slots;
 };
 
 // Workgroups of a main-kernel launch: one per work item and head chunk;

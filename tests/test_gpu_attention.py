@@ -483,3 +483,38 @@ def test_score_jumps_around_the_running_reference(dtype, partition_size):
     got = _paged_on_gpu(p, dtype, scale, Hkv, kernel="mfma", partition_size=partition_size)
     want = p.run(oracle.paged_attention_decode, scale, Hkv)
     assert_rows_close(widen(got), want, dtype, f"score jumps ({dtype}, partition {partition_size})")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,B,window,part", [
+    ("f32", 2, 2, 16, 0, 0), ("f16", 4, 4, 16, 0, 0), ("bf16", 2, 1, 32, 0, 32), ("f16", 16, 1, 8, 0, 0),
+    ("bf16", 4, 2, 64, 40, 0), ("f32", 2, 2, 16, 9, 16), ("bf16", 2, 2, 16, 0, 0)])
+def test_one_launch_decode_step_is_bit_identical(dtype, Hq, Hkv, B, window, part):
+    """Small batches on the vector kernel run the decode step in one launch:
+    the attention workgroups store the new tokens and read them from the
+    inputs.  Caches and outputs must equal reshape_and_cache followed by
+    paged_attention_decode bit for bit, with windows, split partitions, more
+    than 8 query heads per KV head (head chunks), empty sequences and tokens
+    without a slot."""
+    lens = [5, 17, 0, 33, 64, 1]
+    cfg = DecodeConfig("one_launch", num_seqs=len(lens), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128,
+                       dtype=dtype, block_size=B, lengths="fixed", fixed_lengths=tuple(lens), sliding_window=window)
+    lay = make_layout(cfg, seed=41)
+    host = host_values(lay)
+    say(f"one-launch step {dtype} Hq={Hq} Hkv={Hkv} B={B} window={window} partition={part}")
+    a = DeviceStep.from_host(lay, host)
+    b = DeviceStep.from_host(lay, host)
+    if dtype == "bf16" and Hq == 2 and Hkv == 2:
+        # sequence 3 gets no slot: nothing is stored for it on either path
+        slots = lay.new_slots.copy()
+        slots[3] = -1
+        a.slots = b.slots = ints(slots)
+    a.scatter()
+    out_a = a.attend(partition_size=part, sliding_window=window, kernel="valu")
+    out_b = torch.empty_like(b.q)
+    pkv.decode_step(out_b, b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.slots, b.tables, b.lens, cfg.scale, B,
+                    Hkv, lay.max_context_len, partition_size=part, sliding_window=window, kernel="valu")
+    torch.cuda.synchronize()
+    view = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(a.k_cache.view(view), b.k_cache.view(view))
+    assert torch.equal(a.v_cache.view(view), b.v_cache.view(view))
+    assert torch.equal(out_a.view(view), out_b.view(view))
