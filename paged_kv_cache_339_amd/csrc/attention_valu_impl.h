@@ -22,8 +22,10 @@
 namespace pkv {
 
 // DT: query / output format; KT: cache format (DT, or 8-bit E4M3 codes);
-// NT: key/value loads with the nontemporal hint (see load_kv).
-template <int DT, int KT, int D, int B, int G, int NW, int U, bool NT>
+// NT: key/value loads with the nontemporal hint (see load_kv); FUSE: the
+// instance of one-launch decode steps (AttnParams::new_k set), the only one
+// that carries the new-token store and substitution and their registers.
+template <int DT, int KT, int D, int B, int G, int NW, int U, bool NT, bool FUSE>
 __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   constexpr int ES = Format<KT>::kBytes;
   constexpr int QES = Format<DT>::kBytes;
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
   // substituted: attention then reads the cache, as after a separate store.
   constexpr int kRowPieces = D * ES / 16;
   bool fused = false;
-  if (p.new_k != nullptr) {
+  if (FUSE && p.new_k != nullptr) {
     const int32_t slot = p.new_slots[it.s];
     fused = slot >= 0 && (int64_t)slot < p.num_slots;
     if (fused && it.part == 0 && it.q0 == it.h * p.group && threadIdx.x < kRowPieces) {
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
         const char* vt = vbase + lane_off * ES;
         // Row tail - 1 of the last block is token L - 1: in a one-launch
         // decode step it comes from the step's inputs.
-        const int new_row = (fused && c0 + jj == last) ? tail - 1 : -1;
+        const int new_row = (FUSE && fused && c0 + jj == last) ? tail - 1 : -1;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           kr[u][i] = u32x4{0, 0, 0, 0};
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
           if (row >= first[u] && row < valid[u]) {
             const char* kp = kt + (size_t)i * TPW * D * ES;
             const char* vp = vt + (size_t)i * TPW * D * ES;
-            if (row == new_row) {
+            if (FUSE && row == new_row) {
               const size_t nr = (((size_t)it.s * Hkv + it.h) * D + sub * EPL) * ES;
               kp = p.new_k + nr;
               vp = p.new_v + nr;
@@ -278,8 +280,16 @@ constexpr int valu_unroll() {
 template <int DT, int KT, int D, int B, int G, bool NT>
 hipError_t launch_valu(const AttnParams& p, hipStream_t st) {
   const dim3 grid((unsigned)attn_grid(p));
-  hipLaunchKernelGGL((attn_valu_kernel<DT, KT, D, B, G, kValuWaves, valu_unroll<DT, KT, D, G>(), NT>),
-                     grid, dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
+  constexpr int U = valu_unroll<DT, KT, D, G>();
+  if constexpr (KT == DT) {
+    if (p.new_k != nullptr) {
+      hipLaunchKernelGGL((attn_valu_kernel<DT, KT, D, B, G, kValuWaves, U, NT, true>), grid,
+                         dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((attn_valu_kernel<DT, KT, D, B, G, kValuWaves, U, NT, false>), grid,
+                     dim3(kValuWaves * kWave), PKV_VALU_LDS_PAD, st, p);
   return hipGetLastError();
 }
 
