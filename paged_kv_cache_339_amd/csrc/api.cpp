@@ -331,6 +331,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.new_v = fuse ? append->v : nullptr;
   p.new_slots = fuse ? append->slot_mapping : nullptr;
   p.num_slots = fuse ? append->num_slots : 0;
+  p.store_k_cache = fuse ? append->k_cache : nullptr;
+  p.store_v_cache = fuse ? append->v_cache : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_pending_error();

@@ -57,8 +57,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_valu_kernel(AttnParams p) {
       const size_t src = (((size_t)it.s * Hkv + it.h) * kRowPieces + threadIdx.x) * 16;
       const u32x4 a = load16(p.new_k + src), b = load16(p.new_v + src);
       const size_t dst = ((((size_t)(slot / B) * Hkv + it.h) * B + slot % B) * kRowPieces + threadIdx.x) * 16;
-      store16(reinterpret_cast<char*>(const_cast<void*>(p.k_cache)) + dst, a);
-      store16(reinterpret_cast<char*>(const_cast<void*>(p.v_cache)) + dst, b);
+      store16(p.store_k_cache + dst, a);
+      store16(p.store_v_cache + dst, b);
     }
   }
 

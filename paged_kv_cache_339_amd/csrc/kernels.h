@@ -73,6 +73,8 @@ struct AttnParams {
   const char* new_v;
   const int32_t* new_slots;
   int64_t num_slots;
+  char* store_k_cache;        // the caches, writable (the decode step's own pointers)
+  char* store_v_cache;
 };
 
 // Workgroups of a main-kernel launch: one per work item and head chunk;
