@@ -68,7 +68,8 @@ enum pkv_status {
   PKV_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch */
   PKV_ERR_NO_BLOCKS = -8,   /* block manager: the free list is empty */
   PKV_ERR_STATE = -9,       /* block manager: unknown/duplicate sequence, bad block */
-  PKV_ERR_CAPACITY = -10    /* an output buffer is too small */
+  PKV_ERR_CAPACITY = -10,   /* an output buffer is too small */
+  PKV_ERR_SCRATCH = -11     /* the call needs more than the library's fixed scratch buffer */
 };
 
 /* Human-readable name of a status code (static storage). */
@@ -231,6 +232,37 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                int32_t num_blocks, pkv_dtype dtype,
                                void* workspace, size_t workspace_bytes,
                                const pkv_attn_options* opts, void* stream);
+
+/*
+ * pkv_paged_attention_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments minus the workspace, the same kernels and
+ * bit-identical results.  The work list and split-K partial results live in
+ * one fixed device array of PKV_NOALLOC_SCRATCH_BYTES bytes that the library
+ * reserves on every GPU it runs on, held until the process ends; nothing is
+ * allocated or freed by the call.
+ * The array is shared by every call on one GPU and keeps what the last call
+ * left: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give undefined rows.  Nothing in it needs to start at
+ * zero (the work list and the partials are written before they are read);
+ * opts->reuse_plan reuses the work list the previous call on that GPU left.
+ * A call whose workspace (pkv_paged_attention_workspace_bytes) exceeds the
+ * array is refused with PKV_ERR_SCRATCH before anything runs: the 64 MiB
+ * hold about 250k split-K partial rows of head_dim 128 in a 16-bit format
+ * (D * 2 + 8 bytes each), while an unsplit batch needs only its 8-byte work
+ * list entry per sequence.
+ * The stream's device (the current device for NULL) is the GPU used; the
+ * array's address on it is looked up on the first call there.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale,
+                                       int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int32_t num_blocks, pkv_dtype dtype,
+                                       const pkv_attn_options* opts, void* stream);
 
 /*
  * One decode step in two launches: every sequence's new token is stored as

@@ -20,6 +20,7 @@ from .ops import (
     decode_step,
     gather_kv,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_decode_shared_prefix,
     plan_info,
     reshape_and_cache,
@@ -31,6 +32,6 @@ from .ops import (
 
 __all__ = [
     "BeamSearchCache", "LIB_PATH", "PkvError", "lib", "check", "BlockManager", "copy_blocks", "decode_step", "gather_kv",
-    "paged_attention_decode", "paged_attention_decode_shared_prefix", "plan_info", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
+    "paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_decode_shared_prefix", "plan_info", "reshape_and_cache", "reshape_and_cache_fp8", "swap_blocks", "workspace_bytes",
     "shared_prefix_workspace_bytes",
 ]

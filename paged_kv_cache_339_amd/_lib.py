@@ -10,6 +10,9 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 KV_FORMATS = {"same": 0, "fp8_e4m3": 1}
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 CACHE_POLICIES = {"stream": 0, "keep": 1}
+# Bytes of the fixed device scratch pkv_paged_attention_decode_noalloc uses
+# (PKV_NOALLOC_SCRATCH_BYTES in pkv.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 c_i32, c_f32, c_size, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -53,6 +56,9 @@ def load(path: str = LIB_PATH):
         "pkv_paged_attention_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32,
                                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
                                                       c_vp, c_size, ctypes.POINTER(AttnOptions), c_vp]),
+        "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_i32,
+                                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                              ctypes.c_int, ctypes.POINTER(AttnOptions), c_vp]),
         "pkv_paged_attention_shared_prefix_workspace_bytes": (
             c_size, [c_i32] * 9 + [ctypes.c_int, ctypes.POINTER(AttnOptions)]),
         "pkv_paged_attention_decode_shared_prefix": (

@@ -235,6 +235,7 @@ const char* pkv_status_str(int status) {
     case PKV_ERR_NO_BLOCKS: return "block pool exhausted";
     case PKV_ERR_STATE: return "invalid block manager state or sequence";
     case PKV_ERR_CAPACITY: return "output buffer too small";
+    case PKV_ERR_SCRATCH: return "needs more than the fixed scratch buffer holds";
     default: return "unknown status";
   }
 }
@@ -268,6 +269,47 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
 
 namespace {
 
+// Every host check of a decode call except those on the workspace, which
+// needs plan->ws_bytes bytes (after PKV_OK).
+int decode_checks(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                  int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int32_t num_blocks, pkv_dtype dtype, const pkv_attn_options* opts, Plan* plan) {
+  const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, dtype, opts, plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
+}  // namespace
+
+namespace pkv {
+
+int decode_arg_status(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int32_t num_blocks, pkv_dtype dtype,
+                      const pkv_attn_options* opts, size_t* workspace_bytes) {
+  Plan plan;
+  const int st = decode_checks(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                               block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                               max_blocks_per_seq, max_context_len, num_blocks, dtype, opts, &plan);
+  if (st == PKV_OK) *workspace_bytes = plan.ws_bytes;
+  return st;
+}
+
+}  // namespace pkv
+
+namespace {
+
 // Decode attention; with `append`, the launch that builds the work list also
 // stores every sequence's new token (a decode step in two launches).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -278,15 +320,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append,
                 const int32_t* seq_start = nullptr, float* lse = nullptr) {
   Plan plan;
-  const int st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, dtype, opts, &plan);
+  const int st = decode_checks(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                               block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                               max_blocks_per_seq, max_context_len, num_blocks, dtype, opts, &plan);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL;
-  if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
-  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PKV_ERR_ALIGN;
   if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 

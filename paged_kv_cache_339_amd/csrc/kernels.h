@@ -105,6 +105,16 @@ bool launch_attention_mfma_keep(const AttnParams& p, pkv_dtype dt, pkv_dtype kv,
                                 int block_size, int cap, hipStream_t stream, hipError_t* err);
 hipError_t launch_attention_plan(const AttnParams& p, int block_size, hipStream_t stream);
 
+// Host checks of pkv_paged_attention_decode except those on the workspace:
+// PKV_OK (then *workspace_bytes = what the call needs) or the status the call
+// would return.  Touches neither the runtime nor any pointer.
+int decode_arg_status(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int32_t num_blocks, pkv_dtype dtype,
+                      const pkv_attn_options* opts, size_t* workspace_bytes);
+
 // New tokens of a decode step (one per sequence), stored by the launch that
 // builds the work list.
 struct AppendArgs {

@@ -148,6 +148,31 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                                   num_kv_heads, max_context_len, partition_size=0, kernel="auto", stream=None,
+                                   main_events=None, sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0,
+                                   reuse_plan=False, cache_policy="stream"):
+    """paged_attention_decode with no workspace: the work list and split-K
+    partials live in the library's fixed device scratch (NOALLOC_SCRATCH_BYTES
+    per GPU, shared by every call on that GPU: calls that overlap in time
+    race).  Nothing is allocated.  Raises PkvError (status -11) when the call
+    needs more than the scratch holds."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens, block_size, num_kv_heads,
+                            kv_format)
+    opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan,
+                    cache_policy)
+    st = lib.pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), B, Hkv, S, Hq, D, block_tables.shape[1], int(max_context_len), N, dtype_code(q),
+        ctypes.byref(opts), _stream(stream))
+    check(st, "paged_attention_decode_noalloc")
+    return out
+
+
 def shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
                                   num_groups, group_size, max_prefix_len, dtype_code_, partition_size=0,
                                   kernel="auto", kv_format="same", k_scale=1.0, v_scale=1.0, cache_policy="stream"):

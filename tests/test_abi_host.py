@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_status_strings():
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = pkv.lib.pkv_status_str(code).decode()
         assert s and s != "unknown status"
     assert pkv.lib.pkv_status_str(-99).decode() == "unknown status"
@@ -319,3 +319,38 @@ def test_shared_prefix_partition_suits_both_passes():
     assert shared(dtype=2, Hq=2, Hkv=2, Gs=8, opts=ctypes.byref(opts)) == -6
     bad = AttnOptions(24, 0, None, None)                     # not a multiple of the block size
     assert shared(dtype=2, opts=ctypes.byref(bad)) == -2
+
+
+def noalloc(**over):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, scale=0.125, B=32, Hkv=8,
+                S=4096, Hq=64, D=128, M=1024, max_ctx=32768, N=200000, dtype=2,
+                opts=AttnOptions(512, 0, None, None, 0, 0, 1.0, 1.0, 0, 0), stream=None)
+    args.update(over)
+    a = args
+    return pkv.lib.pkv_paged_attention_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["tables"], a["lens"],
+                                                      a["scale"], a["B"], a["Hkv"], a["S"], a["Hq"], a["D"],
+                                                      a["M"], a["max_ctx"], a["N"], a["dtype"],
+                                                      ctypes.byref(a["opts"]), a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), -11),                                    # 16.7M split-K partial rows: far past the scratch
+    (dict(S=300), -11),
+    (dict(out=None), -1), (dict(D=96), -4), (dict(Hq=60), -2), (dict(dtype=3), -3),
+    (dict(q=ctypes.c_void_p(0x1008)), -5), (dict(S=0), 0),
+])
+def test_noalloc_host_checks(over, status):
+    """Argument errors as the workspace call reports them, and a call that
+    needs more than the fixed scratch refused with PKV_ERR_SCRATCH, all before
+    any runtime call (none reaches the GPU here)."""
+    assert noalloc(**over) == status
+
+
+def test_noalloc_scratch_size_matches_header():
+    from paged_kv_cache_339_amd._lib import NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == NOALLOC_SCRATCH_BYTES
+    # The largest unsplit batch fits: its workspace is the header and the work list.
+    need = pkv.workspace_bytes(65536, 64, 8, 128, 32, 32768, 2, 0)
+    assert 0 < need <= NOALLOC_SCRATCH_BYTES
