@@ -123,6 +123,20 @@ struct MergeSmem {
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
+// Eight values rounded to a 16-bit format DT (nearest even), packed in
+// element order into 16 bytes.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_row8(const float (&x)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = DT == PKV_F16 ? narrow_f16(x[2 * k]) : narrow_bf16(x[2 * k]);
+    const uint32_t hi = DT == PKV_F16 ? narrow_f16(x[2 * k + 1]) : narrow_bf16(x[2 * k + 1]);
+    w[k] = lo | (hi << 16);
+  }
+  return w;
+}
+
 // Eight consecutive elements of one row, rounded to the stored format and
 // written with one 16-byte store (two for fp32 rows); NTS: with the
 // nontemporal hint.
@@ -137,13 +151,7 @@ __device__ __forceinline__ void store_row8(void* base, size_t idx, const float (
       else *reinterpret_cast<f32x4v*>(dst + 4 * h) = v;
     }
   } else {
-    u32x4 w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = DT == PKV_F16 ? narrow_f16(x[2 * k]) : narrow_bf16(x[2 * k]);
-      const uint32_t hi = DT == PKV_F16 ? narrow_f16(x[2 * k + 1]) : narrow_bf16(x[2 * k + 1]);
-      w[k] = lo | (hi << 16);
-    }
+    const u32x4 w = pack_row8<DT>(x);
     u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + idx);
     if constexpr (NTS) __builtin_nontemporal_store(w, dst);
     else *dst = w;
@@ -172,18 +180,46 @@ __device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8
   }
 }
 
+// Raw-buffer descriptor word 3 on gfx9: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of a buffer store: sc1 (system-coherent scope), the data
+// written through to memory.
+constexpr int kStoreSc1 = 16;
+
+// Eight consecutive elements of a split-K partial row, stored with the sc1
+// policy into the workgroup's run of partial rows (`run`, `run_bytes`; a
+// wave-uniform base, so the descriptor lives in scalar registers); `idx`:
+// element offset in the run.
+template <int DT>
+__device__ __forceinline__ void store_partial8(void* run, uint32_t run_bytes, int idx, const float (&x)[8]) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(run, 0, run_bytes, kBufferWord3);
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 v = u32x4{__builtin_bit_cast(uint32_t, x[4 * h]), __builtin_bit_cast(uint32_t, x[4 * h + 1]),
+                            __builtin_bit_cast(uint32_t, x[4 * h + 2]), __builtin_bit_cast(uint32_t, x[4 * h + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (idx + 4 * h) * 4, 0, kStoreSc1);
+    }
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(pack_row8<DT>(x), rs, idx * 2, 0, kStoreSc1);
+  }
+}
+
 // After every wave has put its (m, l, o) for the chunk's heads into `sm`:
 // merge the waves and store.  A sequence with one partition gets its final
 // output rows; otherwise the partition's normalised output and (m, l) go to
 // the workspace for the reduce kernel, laid out [S, Hkv*C, P, cap, D] (in
 // the output format) and [S, Hkv*C, P, cap, 2] (fp32): one workgroup's rows
 // form one contiguous run, and the partitions of a (sequence, chunk) follow
-// each other.  Written into the saturated read stream of the other
-// workgroups, these bytes cost far more than their share of the traffic, so
-// they are kept as narrow as the output itself.  NT: the partials carry the
-// nontemporal hint, as the key/value loads do (on a 64-way split GQA layer
-// the main kernel ran 2% faster; with plain loads, whose blocks are meant
-// to stay in cache, plain stores measured faster).
+// each other.  Measured on the 512-token split of the 70B-style GQA layer,
+// these rows cost ~12% of the main kernel although they are 0.8% of its
+// bytes: the cost goes with the partial lines that leave L2 (the same
+// stores aimed at a 4 KiB run that stays in L2 cost nothing, at a 64 MB run
+// as much as at the whole workspace), so they are kept as narrow as the
+// output itself.  NT (streamed key/value loads): the rows are written
+// through with the sc1 policy, 1.2% faster on that layer than nontemporal
+// or plain stores; with plain loads, whose blocks are meant to stay in
+// cache, plain stores measured faster.
 template <int DT, int D, int G, int NW, bool NT>
 __device__ __forceinline__ void merge_and_store(const AttnParams& p, const MergeSmem<D, G, NW>& sm,
                                                 const WorkItem& it, int nparts) {
@@ -219,7 +255,12 @@ __device__ __forceinline__ void merge_and_store(const AttnParams& p, const Merge
     } else {
       const size_t row0 =
           (((size_t)it.s * p.num_kv_heads * p.chunks + it.slot) * p.max_parts + it.part) * G;
-      store_row8<DT, NT>(p.ws_o, (row0 + g) * D + d, r);
+      if constexpr (NT) {
+        constexpr int ES = DT == PKV_F32 ? 4 : 2;
+        store_partial8<DT>(static_cast<char*>(p.ws_o) + row0 * D * ES, (uint32_t)(G * D * ES), g * D + d, r);
+      } else {
+        store_row8<DT, false>(p.ws_o, (row0 + g) * D + d, r);
+      }
       if (d == 0) {
         const f32x2v ml = f32x2v{M, bad ? __builtin_nanf("") : tot};
         f32x2v* dst = reinterpret_cast<f32x2v*>(p.ws_ml + (row0 + g) * 2);
