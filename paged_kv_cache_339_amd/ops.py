@@ -2,7 +2,8 @@
 
 Device tensors must be contiguous and on the GPU; the stream defaults to
 torch's current stream.  Nothing here computes: each call is one library
-call (plus, at most, a workspace allocation when the caller passes none).
+call (plus, at most, a workspace allocation when the caller passes none,
+marked as used by the call's stream).
 """
 from __future__ import annotations
 
@@ -99,12 +100,36 @@ def _check_attention_shapes(out, q, k_cache, v_cache, block_tables, context_lens
         raise ValueError("block_tables must be [S, M] and context_lens [S]")
 
 
+def _torch_stream(stream):
+    """torch stream object for a `stream` argument (None: None)."""
+    torch = _torch()
+    if stream is None:
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _temp_workspace(need, device, stream):
+    """A workspace the wrapper allocates for one call.  torch's caching
+    allocator ties the block to the current stream, but the library's kernels
+    run on `stream`: the block is marked as used there too, so the allocator
+    does not hand its bytes to another allocation before that stream's work
+    (the plan, main and reduce kernels) is done."""
+    torch = _torch()
+    workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ts = _torch_stream(stream)
+    if ts is not None:
+        workspace.record_stream(ts)
+    return workspace
+
+
 def _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, device,
-               sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0):
+               sliding_window=0, kv_format="same", k_scale=1.0, v_scale=1.0, stream=None):
     need = workspace_bytes(S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, sliding_window,
                            kv_format, k_scale, v_scale)
     if need and workspace is None:
-        workspace = _torch().empty(need, dtype=_torch().uint8, device=device)
+        workspace = _temp_workspace(need, device, stream)
     return workspace
 
 
@@ -136,7 +161,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                             kv_format)
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
-                           sliding_window, kv_format, k_scale, v_scale)
+                           sliding_window, kv_format, k_scale, v_scale, stream)
     opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan,
                     cache_policy)
     st = lib.pkv_paged_attention_decode(
@@ -212,7 +237,7 @@ def paged_attention_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
         need = shared_prefix_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, Gn, Gs, max_prefix_len, code,
                                              partition_size, kernel, kv_format, k_scale, v_scale, cache_policy)
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _temp_workspace(need, q.device, stream)
     opts = _options(partition_size, kernel, main_events, 0, kv_format, k_scale, v_scale, reuse_plan, cache_policy)
     st = lib.pkv_paged_attention_decode_shared_prefix(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -246,7 +271,7 @@ def decode_step(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tabl
         raise ValueError("slot_mapping must be [num_seqs]")
     code = dtype_code(q)
     workspace = _workspace(workspace, S, Hq, Hkv, D, B, max_context_len, code, partition_size, kernel, q.device,
-                           sliding_window, kv_format, k_scale, v_scale)
+                           sliding_window, kv_format, k_scale, v_scale, stream)
     opts = _options(partition_size, kernel, main_events, sliding_window, kv_format, k_scale, v_scale, reuse_plan,
                     cache_policy)
     st = lib.pkv_decode_step(
