@@ -66,3 +66,19 @@ def test_beam_groups_share_the_prompt_blocks_at_every_step(R, W, P, steps, B):
                      refcount=lambda b: cache.bm.refcount(b))
         assert len(ids) == R * W
     cache.close()
+
+
+def test_block_manager_builds_the_sampling_batch_at_full_shape():
+    """The shared-prefix sampling workload at full shape (64 prompts x 8
+    samples, 1000-token prompts, tails up to 512), built by prefill, fork and
+    one append per sample per decode step: the C++ block manager equals the
+    oracle twin on every slot, pair and table, and the divergence step yields
+    the 448 copies (7 per prompt) the workload states."""
+    from synthetic import CONFIGS, make_layout
+    from tests.cow_replay import check_divergence_structure, replay_shared_prefix
+    cfg = CONFIGS[5]
+    lay = make_layout(cfg, seed=5)
+    rep = replay_shared_prefix(cfg, lay)
+    check_divergence_structure(cfg, rep)
+    assert len(rep.div_pairs) == 448
+    assert np.array_equal(rep.lens, lay.context_lens)
