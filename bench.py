@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
-"""Benchmark of one paged-attention decode step on one MI355X.
+"""Benchmark of the paged-attention decode step on one MI355X.
 
-A step is the whole decode hot path for one batch: copy_blocks when the
-workload has copy-on-write pairs, then pkv_decode_step, which stores the
-token each sequence appends (reshape_and_cache) in the launch that builds
-the attention work list, and runs paged decode attention over all cached
-tokens (main kernel, plus the split-K reduce when partitions split a
-sequence).  On the shared-prefix workload the step is copy_blocks,
-reshape_and_cache and pkv_paged_attention_decode_shared_prefix, which reads
-each prompt's shared blocks once for all its samples (--per-sample-prefix:
-the plain decode step instead).  Inputs are synthetic, seeded, N(0, 1), and
-resident in HBM before timing starts.  The default workload is a
-Llama-2-7B-shaped layer: batch 64, 32 heads, head_dim 128, fp16 KV cache in
-16-token blocks, context lengths uniform in [128, 2048], blocks scattered at
-random over a pool 1.2x the need.
+A step is the decode hot path for one batch: pkv_decode_step, which stores
+the token each sequence appends (reshape_and_cache) in the launch that
+builds the attention work list, then runs paged decode attention over all
+cached tokens (main kernel, plus the split-K reduce when partitions split a
+sequence).  On the shared-prefix workload the step is reshape_and_cache and
+pkv_paged_attention_decode_shared_prefix, which reads each prompt's shared
+blocks once for all its samples (--per-sample-prefix: the plain decode step
+instead); that batch is built the way a server builds it (block manager,
+stores, and the copy-on-write copies made by copy_blocks at the divergence
+step), and the divergence step's copy_blocks is timed on its own.  Inputs
+are synthetic, seeded, N(0, 1), and resident in HBM before timing starts.
+
+Default run: the headline workload is the largest one that fits one GPU, a
+70B-style grouped-query layer (batch 256, 64 query / 8 KV heads, head_dim
+128, bf16, 32-token blocks, context lengths uniform in [1024, 32768], split-K
+partitions of 512 tokens + the reduce kernel); the same JSON line carries
+`per_config` with the tiny fp32 step, the Llama-2-7B and -13B layers and the
+shared-prefix sampling batch at the same --steps and --warmup.
 
 Prints ONE JSON line:
   value        KV GB/s read per step (sum(L) * Hkv * D * 2 * bytes / step time),
@@ -28,6 +33,8 @@ Prints ONE JSON line:
                in K steps
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
                on this host's cores (a reported baseline, not the target)
+  per_config   (default run) the other workloads' step time, GB/s, % of peak,
+               seq*heads/s and main-kernel roofline fraction
 
     python bench.py [--steps K] [--warmup W] [--config N] [--gpus 1]
 """
@@ -532,53 +539,151 @@ def swap_bench(args):
                       "swap_out": res["out"], "swap_in": res["in"]}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS) + sorted(BEAM_CONFIGS))
-    ap.add_argument("--partition-size", type=int, default=-1,
-                    help="split-K partition in tokens (0 = library default; -1 = the workload's own)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--placement", default=None, choices=["shuffled", "contiguous"],
-                    help="contiguous: each sequence's blocks adjacent and in order (the cost of paging)")
-    ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
-    ap.add_argument("--tp-share", type=int, default=1,
-                    help="N > 1: one GPU's share of N-way tensor parallelism (heads / N)")
-    ap.add_argument("--cache-policy", default=None, choices=["stream", "keep"],
-                    help="override the workload's key/value load policy")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--per-sample-prefix", action="store_true",
-                    help="shared-prefix workloads: read the shared prompt blocks once per sample (plain decode "
-                         "step, cache-resident re-reads) instead of once per prompt for all its samples "
-                         "(pkv_paged_attention_decode_shared_prefix, the default)")
-    ap.add_argument("--swap", action="store_true",
-                    help="instead of the decode step, time pkv_swap_blocks of a quarter of the workload's "
-                         "blocks to a pinned host pool and back (PCIe-bound)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="instead of the decode step, run copy_blocks over a known number of bytes "
-                         "(the reference reading for the HBM traffic counters)")
-    args = ap.parse_args()
+W_COPY = 3          # untimed copy_blocks launches before the timed ones
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py measures one GPU only: the library has no multi-GPU path "
-            "(the decode step shards by KV head or by sequence with no exchange); run with --gpus 1")
-        sys.exit(2)
 
-    if args.calibrate_copy:
-        calibrate_copy(args.steps)
-        return
-    if args.config in BEAM_CONFIGS:
-        beam_bench(args)
-        return
-    if args.swap:
-        swap_bench(args)
-        return
+def shared_prefix_state(cfg, layout, dev, seed: int) -> dict:
+    """The shared-prefix sampling batch built the way a server builds it.
 
-    cfg = CONFIGS[args.config]
+    The host block manager (pkv_bm_*, the C++ control plane) prefills each
+    prompt, forks it for the samples, and appends their tokens one decode
+    step at a time (every sample one token per step).  The library stores
+    every token (pkv_reshape_and_cache) and, at the divergence step, makes the
+    copy-on-write copies of each prompt's partial last block (pkv_copy_blocks)
+    before any sample token lands in them.  The pool size and the context
+    lengths are the workload's (`layout`); values are N(0, 1) drawn on the GPU.
+    The last token of each sequence is left for the timed step to store."""
+    import torch
+    import paged_kv_cache_339_amd as pkv
+
+    S, spp, P, B = len(layout.context_lens), cfg.samples_per_prompt, cfg.prompt_len, cfg.block_size
+    Hq, Hkv, D, N = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, layout.num_blocks
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed * 64 + 9)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(tdt)
+
+    def ints(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    # Slots that hold no token stay all-ones bits (NaN in every format).
+    kc = torch.full((N, Hkv, B, D), -1, dtype=torch.int16 if tdt != torch.float32 else torch.int32,
+                    device=dev).view(tdt)
+    vc = kc.clone()
+    bm = pkv.BlockManager(N, B, S, free_order=layout.pool_order)
+    prompt_slots = []
+    for p in range(S // spp):
+        bm.add_seq(p * spp)
+        sl, pr = bm.append_batch([p * spp] * P)
+        assert len(pr) == 0
+        prompt_slots.append(sl)
+    prompt_slots = np.concatenate(prompt_slots)
+    pkv.reshape_and_cache(randn(len(prompt_slots), Hkv, D), randn(len(prompt_slots), Hkv, D), kc, vc,
+                          ints(prompt_slots))
+    for p in range(S // spp):
+        for k in range(1, spp):
+            bm.fork(p * spp, p * spp + k)
+    tails = layout.context_lens.astype(np.int64) - P
+    assert tails.min() >= 1
+    stored, last = [], np.full(S, -1, dtype=np.int32)
+    div_pairs = None
+    for t in range(int(tails.max())):
+        seqs = np.nonzero(tails > t)[0].astype(np.int32)
+        sl, pr = bm.append_batch(seqs)
+        if t == 0:
+            div_pairs = pr
+            if len(pr):
+                pkv.copy_blocks(kc, vc, ints(pr))          # before any sample token is stored
+        else:
+            assert len(pr) == 0
+        fin = tails[seqs] == t + 1
+        last[seqs[fin]] = sl[fin]
+        stored.append(sl[~fin])
+    stored = np.concatenate(stored)
+    pkv.reshape_and_cache(randn(len(stored), Hkv, D), randn(len(stored), Hkv, D), kc, vc, ints(stored))
+    M = layout.block_tables.shape[1]
+    tables, lens = bm.export(np.arange(S), M)
+    bm.close()
+    assert np.array_equal(lens, layout.context_lens) and (last >= 0).all()
+    torch.cuda.synchronize()
+    return {"q": randn(S, Hq, D), "k_cache": kc, "v_cache": vc, "k_new": randn(S, Hkv, D),
+            "v_new": randn(S, Hkv, D), "tables": tables, "lens": lens, "slots": last,
+            "pairs": div_pairs}
+
+
+def launch_floor(steps: int) -> dict:
+    """The shortest back-to-back library launch on this GPU: K launches of a
+    one-token pkv_reshape_and_cache (head_dim 64, two heads, fp32) through
+    the C ABI with prepared arguments, as the timed steps are issued, between
+    two events.  The latency floor a tiny decode step sits on."""
+    import torch
+    from paged_kv_cache_339_amd._lib import lib
+    dev = torch.device("cuda:0")
+    k = torch.zeros((1, 2, 64), dtype=torch.float32, device=dev)
+    kc = torch.zeros((4, 2, 16, 64), dtype=torch.float32, device=dev)
+    vc = torch.zeros_like(kc)
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    vp = ctypes.c_void_p
+    a_ = (vp(k.data_ptr()), vp(k.data_ptr()), vp(kc.data_ptr()), vp(vc.data_ptr()), vp(slot.data_ptr()),
+          1, 2, 64, 16, 4, 0, vp(stream))
+    for _ in range(5):
+        assert lib.pkv_reshape_and_cache(*a_) == 0
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    a, b = ev.create(), ev.create()
+    ev.record(a, stream)
+    for _ in range(steps):
+        lib.pkv_reshape_and_cache(*a_)
+    ev.record(b, stream)
+    us = ev.ms(a, b) * 1e3 / steps
+    ev.close()
+    return {"us": round(us, 2),
+            "what": "one-token reshape_and_cache through the C ABI, K back-to-back launches between two events"}
+
+
+def per_config_entry(r: dict) -> dict:
+    """The per-workload summary carried beside the headline."""
+    keys = ("ms_per_step", "value", "unit", "pct_hbm_peak", "seq_heads_per_s", "attention_main_us")
+    e = {k: r[k] for k in keys}
+    e["config"] = {k: r["config"][k] for k in ("batch", "q_heads", "kv_heads", "head_dim", "block_size",
+                                               "kv_dtype", "partition_tokens", "partitions_per_seq", "kernel",
+                                               "step")}
+    rf = r["roofline"]
+    e["main_kernel"] = {k: rf[k] for k in ("kernel", "achieved", "frac", "bytes_per_launch", "timing",
+                                           "rocprof_avg_us", "traffic")}
+    for k in ("grouped_prefix", "copy_blocks", "launch_floor"):
+        if k in r:
+            e[k] = r[k]
+    return e
+
+
+def suite(args):
+    """The default run: the headline workload (the largest single-GPU one,
+    the 70B-style GQA layer at its stated 512-token split-K with the reduce
+    kernel) with its roofline and CPU baseline, and in the same JSON line the
+    other workloads (tiny fp32, Llama-2-7B and -13B layers, shared-prefix
+    sampling) at the same steps and warmup."""
+    import torch
+    head = decode_workload(args, 4, not args.no_cpu_baseline)
+    torch.cuda.empty_cache()
+    per = {}
+    for idx in (1, 2, 3, 5):
+        r = decode_workload(args, idx, False)
+        if idx == 1:
+            r["launch_floor"] = launch_floor(args.steps)
+        per[r["config"]["workload"]] = per_config_entry(r)
+        torch.cuda.empty_cache()
+    head["per_config"] = per
+    return head
+
+
+def decode_workload(args, idx: int, with_cpu: bool) -> dict:
+    """One decode workload: K timed steps, the main kernel's duration, and
+    (with_cpu) the oracle's CPU baseline.  Returns the result record."""
+    cfg = CONFIGS[idx]
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
     # The workload's name, tagged with every change from its stated form.
     tag = cfg.name
@@ -612,7 +717,7 @@ def main():
         cfg = cfg.scaled(partition_size=part)
     if part != cfg.partition_size:
         tag += f"_partition{part or 'auto'}"
-    seed = args.config if args.seed is None else args.seed
+    seed = idx if args.seed is None else args.seed
     layout = make_layout(cfg, seed=seed)
     S, Hq, Hkv, D, B = len(layout.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     es = DTYPE_BYTES[cfg.dtype]
@@ -621,7 +726,7 @@ def main():
         f"pool={layout.num_blocks} blocks KV/step={step_kv / 1e9:.3f} GB")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, layout, args.cpu_seconds)
         log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} cores")
@@ -635,19 +740,22 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, kc, vc, kn, vn = device_values(layout, device=dev)
 
     def ints(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
+    extra = {}
+    cow = None
+    if cfg.lengths == "shared_prefix":
+        # Built as a server builds it: block manager, stores, and the
+        # copy-on-write copies made by copy_blocks at the divergence step.
+        st = shared_prefix_state(cfg, layout, dev, seed)
+        q, kc, vc, kn, vn = st["q"], st["k_cache"], st["v_cache"], st["k_new"], st["v_new"]
+        layout.block_tables, layout.context_lens, layout.new_slots = st["tables"], st["lens"], st["slots"]
+        cow = st["pairs"]
+    else:
+        q, kc, vc, kn, vn = device_values(layout, device=dev)
     tables, lens, slots = ints(layout.block_tables), ints(layout.context_lens), ints(layout.new_slots)
-    # Copy-on-write pairs into spare blocks (destinations distinct from every source).
-    n_pairs = len(layout.cow_pairs)
-    pairs = None
-    if n_pairs:
-        spare = layout.pool_order[layout.used_blocks:layout.used_blocks + n_pairs]
-        assert len(spare) == n_pairs, "pool has no room for the copy-on-write destinations"
-        pairs = ints(np.stack([layout.cow_pairs[:, 0], spare], axis=1))
     out = torch.empty_like(q)
     code = dtype_code(q)
     max_ctx = layout.max_context_len
@@ -667,10 +775,29 @@ def main():
 
     ev = HipEvents()
     vp = ctypes.c_void_p
-    copy_args = None
-    if pairs is not None:
-        copy_args = (vp(kc.data_ptr()), vp(vc.data_ptr()), vp(pairs.data_ptr()), n_pairs, Hkv, B, D,
-                     layout.num_blocks, dtype_code(kc), vp(stream))
+    if cow is not None:
+        # The divergence step's copies, timed on their own: the same sources
+        # copied into blocks no table names (the real copies were made once,
+        # in setup, before the samples' tokens landed in them).
+        used = set(np.unique(layout.block_tables[layout.block_tables >= 0]).tolist())
+        free = np.array([b for b in range(layout.num_blocks) if b not in used][:len(cow)], dtype=np.int64)
+        assert len(free) == len(cow), "pool has no room for a second set of copy destinations"
+        cpairs = ints(np.stack([cow[:, 0], free], axis=1))
+        cargs = (vp(kc.data_ptr()), vp(vc.data_ptr()), vp(cpairs.data_ptr()), len(cow), Hkv, B, D,
+                 layout.num_blocks, dtype_code(kc), vp(stream))
+        for _ in range(W_COPY):
+            assert lib.pkv_copy_blocks(*cargs) == 0
+        c0, c1 = ev.create(), ev.create()
+        ev.record(c0, stream)
+        for _ in range(args.steps):
+            assert lib.pkv_copy_blocks(*cargs) == 0
+        ev.record(c1, stream)
+        copy_us = ev.ms(c0, c1) * 1e3 / args.steps
+        moved = 2 * 2 * len(cow) * Hkv * B * D * DTYPE_BYTES[cfg.kv_dtype]      # read + written, K and V
+        extra["copy_blocks"] = {"pairs": int(len(cow)), "us": round(copy_us, 2),
+                                "bytes_moved": int(moved), "GBps": round(moved / copy_us / 1e3, 1),
+                                "timing": "K back-to-back launches between two events",
+                                "note": "64 sources copied 7 times each: repeated source reads come from cache"}
 
     def step_args(opts):
         """pkv_decode_step: store each sequence's new token and attend."""
@@ -708,9 +835,6 @@ def main():
     warm_args = step_args(plain)
 
     def step(a):
-        if copy_args is not None:
-            st = lib.pkv_copy_blocks(*copy_args)
-            assert st == 0, st
         if grouped:
             # The new tokens' store, then attention with each prompt's shared
             # blocks read once for its samples.
@@ -773,7 +897,6 @@ def main():
     first = np.maximum(0, lens64 - win) // B if win > 0 else np.zeros_like(lens64)
     nblk = -(-lens64 // B) - first                    # table entries read per (sequence, KV head)
     alg_bytes = step_kv + 2 * S * Hq * D * es + int(nblk.sum()) * 4 * Hkv + S * 4   # es: q / out format
-    extra = {}
     if grouped:
         # The timed kernel is the pass over each sequence's own tokens
         # [P_s, L_s); the shared prefixes are read by the grouped pass.
@@ -782,11 +905,11 @@ def main():
         own_blk = -(-lens64 // B) - prefix_np // B
         alg_bytes = int(own.sum()) * Hkv * D * 2 * kvs + 2 * S * Hq * D * es + int(own_blk.sum()) * 4 * Hkv + S * 8
         pre_tokens = int(prefix_np[members_np[:, 0]].sum())
-        extra = {"grouped_prefix": {
+        extra["grouped_prefix"] = {
             "groups": Gn, "members": Gs, "prefix_tokens": int(prefix_np[0]),
             "unique_kv_bytes_per_step": (pre_tokens + int(own.sum())) * Hkv * D * 2 * kvs,
             "prefix_pass_kv_bytes": pre_tokens * Hkv * D * 2 * kvs,
-            "own_pass_kv_bytes": int(own.sum()) * Hkv * D * 2 * kvs}}
+            "own_pass_kv_bytes": int(own.sum()) * Hkv * D * 2 * kvs}
     achieved = alg_bytes / main_s / 1e9
     kv_gbps = step_kv / step_s / 1e9
     result = {
@@ -800,22 +923,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # The arithmetic the main kernel computes in: fp32 on the vector ALUs;
-        # 16-bit operands (8-bit codes widened to them) with fp32 accumulation
-        # on the matrix cores.
-        "dtype": "f32" if kernel_used == "valu" else cfg.dtype,
+        # The workload's query / output format (caches: config.kv_dtype); the
+        # arithmetic is in "compute".
+        "dtype": cfg.dtype,
+        "compute": ("fp32 on the vector ALUs" if kernel_used == "valu" else
+                    f"{cfg.dtype} operands (8-bit codes widened to them) on the matrix cores, fp32 accumulation"),
         "data": "synthetic",
         "config": {
             "workload": tag,
             "batch": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": B,
-            "kv_dtype": cfg.kv_dtype, "context_lens": LENGTH_DESC[args.config],
+            "kv_dtype": cfg.kv_dtype, "context_lens": LENGTH_DESC[idx],
             "sum_context_tokens": int(layout.context_lens.sum()), "pool_blocks": layout.num_blocks,
             "kv_bytes_per_step": step_kv, "partition_size": part, "partition_tokens": chosen_part,
             "partitions_per_seq": parts_per_seq, "kernel": kernel_used,
             "sliding_window": win, "kv_format": cfg.kv_format, "cache_policy": cfg.cache_policy,
-            "step": ("copy_blocks + " if copy_args else "") + (
-                "reshape_and_cache + decode_shared_prefix (grouped prefix pass, own-token pass, merge)" if grouped
-                else "decode_step (new-token store + plan, attention)"),
+            "step": ("reshape_and_cache + decode_shared_prefix (grouped prefix pass, own-token pass, merge)"
+                     if grouped else "decode_step (new-token store + plan, attention)"),
         },
         **extra,
         "pct_hbm_peak": round(100 * kv_gbps / HBM_PEAK_GBPS, 2),
@@ -836,6 +959,63 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=None, choices=sorted(CONFIGS) + sorted(BEAM_CONFIGS),
+                    help="one workload; default: the headline (workload 4) with workloads 1, 2, 3 and 5 "
+                         "in per_config")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="split-K partition in tokens (0 = library default; -1 = the workload's own)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--placement", default=None, choices=["shuffled", "contiguous"],
+                    help="contiguous: each sequence's blocks adjacent and in order (the cost of paging)")
+    ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
+    ap.add_argument("--tp-share", type=int, default=1,
+                    help="N > 1: one GPU's share of N-way tensor parallelism (heads / N)")
+    ap.add_argument("--cache-policy", default=None, choices=["stream", "keep"],
+                    help="override the workload's key/value load policy")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--per-sample-prefix", action="store_true",
+                    help="shared-prefix workloads: read the shared prompt blocks once per sample (plain decode "
+                         "step, cache-resident re-reads) instead of once per prompt for all its samples "
+                         "(pkv_paged_attention_decode_shared_prefix, the default)")
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of the decode step, time pkv_swap_blocks of a quarter of the workload's "
+                         "blocks to a pinned host pool and back (PCIe-bound)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="instead of the decode step, run copy_blocks over a known number of bytes "
+                         "(the reference reading for the HBM traffic counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU only: the library has no multi-GPU path "
+            "(the decode step shards by KV head or by sequence with no exchange); run with --gpus 1")
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
+    if args.config in BEAM_CONFIGS:
+        beam_bench(args)
+        return
+    if args.swap:
+        if args.config is None:
+            sys.exit("--swap needs --config")
+        swap_bench(args)
+        return
+
+    if args.config is None:
+        result = suite(args)
+    else:
+        result = decode_workload(args, args.config, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
 
 
