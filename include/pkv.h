@@ -48,8 +48,11 @@ extern "C" {
 
 /* Element formats.  PKV_FP8_E4M3 (OCP 8-bit E4M3, finite: bias 7, no
  * infinities, S.1111.111 = NaN, largest magnitude 448) is a KV-cache format
- * only: queries and outputs stay f32/f16/bf16. */
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
+ * only: queries and outputs stay f32/f16/bf16.  A pkv_dtype argument is a
+ * plain 32-bit integer, so any value a caller passes is representable and
+ * an unknown one is refused with PKV_ERR_DTYPE. */
+typedef int32_t pkv_dtype;
+enum pkv_dtype_value { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 };
 
 /* KV-cache format of the attention calls (pkv_attn_options.kv_format). */
 enum pkv_kv_format {

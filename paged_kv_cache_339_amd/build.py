@@ -83,8 +83,63 @@ def build(jobs: int | None = None, verbose: bool = True, out: str = LIB, build_d
     return out
 
 
+# Host-code sanitizer build (CPU tests only): the C ABI's argument checks and
+# split-K planning (api.cpp, noalloc.hip) and the host block manager
+# (block_manager.cpp) compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer, linked with the regular objects of the kernel
+# sources (whose host code only launches).
+# The sanitizer flags apply to host code only (-Xarch_host); no GPU code is
+# instrumented.  A process loading the result needs the ASan runtime first
+# (LD_PRELOAD=sanitizer_runtime()).
+SANITIZED_SOURCES = ("api.cpp", "block_manager.cpp", "noalloc.hip")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+SANITIZED_LIB = os.path.join(BUILD, "libpkv_sanitized.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime of the ROCm toolchain."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if out and os.path.isabs(out) and os.path.exists(out):
+        return out
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return found[-1]
+
+
+def build_sanitized(jobs: int | None = None, out: str = SANITIZED_LIB, build_dir: str = BUILD) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sources()
+    plain = [s for s in srcs if os.path.basename(s) not in SANITIZED_SOURCES]
+    san = [s for s in srcs if os.path.basename(s) in SANITIZED_SOURCES]
+    missing = [s for s in plain if not os.path.exists(os.path.join(build_dir, os.path.basename(s) + ".o"))]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    san_dir = os.path.join(build_dir, "sanitized")
+    os.makedirs(san_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda src: _compile(src, build_dir), missing))
+        san_objs = list(ex.map(lambda src: _compile(src, san_dir, SANITIZE_FLAGS), san))
+    objs = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in plain] + san_objs
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--sanitize", action="store_true",
+                    help="build _build/libpkv_sanitized.so: host code under ASan and UBSan (CPU tests)")
     a = ap.parse_args()
-    build(a.jobs)
+    if a.sanitize:
+        print(build_sanitized(a.jobs))
+    else:
+        build(a.jobs)
