@@ -660,16 +660,31 @@ def per_config_entry(r: dict) -> dict:
     return e
 
 
+def run_child(args, idx: int, extra=()) -> dict:
+    """One workload in a process of its own (fresh device memory, as a
+    server allocates its pool once at start-up); its JSON line is returned
+    and its progress lines pass through to stderr."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--config", str(idx), "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--no-cpu-baseline", *extra]
+    if args.seed is not None:
+        cmd += ["--seed", str(args.seed)]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if res.returncode != 0:
+        sys.exit(f"workload {idx} failed (exit {res.returncode})")
+    return json.loads([line for line in res.stdout.splitlines() if line.startswith("{")][-1])
+
+
 def suite(args):
     """The default run: the headline workload (the largest single-GPU one,
     the 70B-style GQA layer at its stated 512-token split-K with the reduce
     kernel) with its roofline and CPU baseline, and in the same JSON line the
     other workloads (tiny fp32, Llama-2-7B and -13B layers, shared-prefix
-    sampling) at the same steps and warmup."""
-    import torch
-    # The oracle baseline first, before the GPU is touched (its worker pool
-    # forks); the headline runs last, so the other workloads' buffers are
-    # not placed after its 22 GB pool (measured 2-4% slower there).
+    sampling) at the same steps and warmup.  This process never touches the
+    GPU: the oracle baseline runs here first (its worker pool forks), then
+    each workload runs in a child process of its own, one after the other.
+    (In one process, a workload allocated after another's buffers had been
+    freed measured 2-4% slower.)"""
     cpu = None
     if not args.no_cpu_baseline:
         cfg = CONFIGS[4]
@@ -677,15 +692,14 @@ def suite(args):
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, layout, args.cpu_seconds)
         log(f"cpu baseline: {cpu['value']} GB/s on {cpu['cores']} cores")
+    head = run_child(args, 4)
+    head["cpu_baseline"] = cpu
     per = {}
     for idx in (1, 2, 3, 5):
-        r = decode_workload(args, idx, False)
-        if idx == 1:
-            r["launch_floor"] = launch_floor(args.steps)
+        r = run_child(args, idx, ["--launch-floor"] if idx == 1 else [])
         per[r["config"]["workload"]] = per_config_entry(r)
-        torch.cuda.empty_cache()
-    head = decode_workload(args, 4, cpu is not None, cpu=cpu)
     head["per_config"] = per
+    head["process_per_workload"] = True
     return head
 
 
@@ -994,6 +1008,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="also time the shortest back-to-back library launch (a one-token reshape_and_cache)")
     ap.add_argument("--per-sample-prefix", action="store_true",
                     help="shared-prefix workloads: read the shared prompt blocks once per sample (plain decode "
                          "step, cache-resident re-reads) instead of once per prompt for all its samples "
@@ -1027,6 +1043,8 @@ def main():
         result = suite(args)
     else:
         result = decode_workload(args, args.config, not args.no_cpu_baseline)
+        if args.launch_floor:
+            result["launch_floor"] = launch_floor(args.steps)
     print(json.dumps(result), flush=True)
 
 
