@@ -5,6 +5,7 @@ pkv_paged_attention_decode's with a caller workspace (same kernels), on two
 calls in a row, the second with a smaller batch, and within the stated
 tolerance of the fp64 oracle."""
 import ctypes
+import dataclasses
 
 import numpy as np
 import pytest
@@ -20,15 +21,20 @@ pytestmark = pytest.mark.gpu
 vp = ctypes.c_void_p
 
 
-def _call(fn, step, out, part, *ws):
+def _call(fn, step, out, part, *ws, reuse=False):
     lay, cfg = step.layout, step.layout.cfg
     S, Hq, D = step.q.shape
-    opts = AttnOptions(part, 0, None, None, 0, 0, 1.0, 1.0, 0, 0)
+    opts = AttnOptions(part, 0, None, None, 0, 0, 1.0, 1.0, 1 if reuse else 0, 0)
     stream = vp(torch.cuda.current_stream().cuda_stream)
     return fn(vp(out.data_ptr()), vp(step.q.data_ptr()), vp(step.k_cache.data_ptr()), vp(step.v_cache.data_ptr()),
               vp(step.tables.data_ptr()), vp(step.lens.data_ptr()), cfg.scale, cfg.block_size, cfg.num_kv_heads,
               S, Hq, D, lay.block_tables.shape[1], lay.max_context_len, lay.num_blocks, dtype_code(step.q),
               *ws, ctypes.byref(opts), stream)
+
+
+def _with_q(step, q):
+    """The same step with other queries (another layer's)."""
+    return dataclasses.replace(step, q=q)
 
 
 def _case(cfg, seed, part):
@@ -70,3 +76,56 @@ def test_noalloc_matches_workspace_call(order):
         want, _, _ = oracle_step(lay, host)
         err = assert_rows_close(widen(got), want, cfg.dtype, f"noalloc {cfg.name}")
         say(f"noalloc {cfg.name}: bit-identical to the workspace call, max row-relative error {err:.2e}")
+
+
+def test_noalloc_calls_captured_in_a_graph_replay_bit_identically():
+    """What the entry point is for: decode calls captured in a HIP graph
+    (torch.cuda.graph), where nothing may be allocated.  Two layers per step
+    (the first builds the work list in the scratch, the second reuses it),
+    512-token split-K partitions (partials and reduce in the scratch too);
+    every replay must equal the workspace call, also after eager calls on the
+    same scratch between the replays."""
+    cfg = CONFIGS[4].scaled(num_seqs=6, len_hi=2500)
+    lay, host, step, need = _case(cfg, 43, 512)
+    S, Hq, D = step.q.shape
+    layers = [step.q, (step.q.view(torch.int16) ^ -0x8000).view(step.q.dtype)]   # second layer: -q
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    refs = []
+    for q in layers:
+        ref = torch.empty_like(q)
+        st = _call(lib.pkv_paged_attention_decode, _with_q(step, q), ref, 512, vp(ws.data_ptr()), ws.numel())
+        assert st == 0, st
+        refs.append(ref)
+    outs = [torch.full_like(step.q, float("nan")) for _ in layers]
+
+    def run():
+        for l, (q, o) in enumerate(zip(layers, outs)):
+            st = _call(lib.pkv_paged_attention_decode_noalloc, _with_q(step, q), o, 512, reuse=l > 0)
+            assert st == 0, st
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):            # warm-up on a side stream, as torch asks before capture
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    eager = [torch.empty_like(step.q) for _ in layers]
+    for replay in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (o, ref) in enumerate(zip(outs, refs)):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), (replay, l)
+        # Eager calls on the same scratch between the replays.
+        for q, e in zip(layers, eager):
+            assert _call(lib.pkv_paged_attention_decode_noalloc, _with_q(step, q), e, 512) == 0
+        torch.cuda.synchronize()
+        for e, ref in zip(eager, refs):
+            assert torch.equal(e.view(torch.int16), ref.view(torch.int16)), replay
+    say(f"noalloc graph: {len(layers)} layers x 3 replays bit-identical to the workspace call (S={S})")
