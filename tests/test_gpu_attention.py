@@ -174,28 +174,12 @@ def test_gqa_matches_replicated_mha_within_tolerance():
     assert_rows_close(widen(g), widen(m), "bf16", "GQA vs MHA")
 
 
-def test_work_list_covers_every_partition_longest_first():
+def _check_work_list(ws, lens, B, part):
     """The plan at the head of the workspace (after a 256-byte header whose
     first int32 is the pair count) names every (sequence, partition) pair of
     the call exactly once: full partitions in sequence order, then the
-    shorter last partitions by non-increasing size, then empty sequences."""
-    rng = np.random.default_rng(17)
-    B, part = 16, 512
-    lens = rng.integers(1, 3000, size=37)
-    lens[[3, 20]] = 0
-    lens[7] = 512
-    lens[9] = 1024
-    cfg = _edge_cfg("bf16", 128, B, 4, 2).scaled(num_seqs=len(lens))
-    lay = make_layout(cfg, 21, lengths=lens)
-    step = DeviceStep.from_host(lay, host_values(lay))
-    max_ctx = int(lens.max())
-    need = pkv.workspace_bytes(len(lens), 4, 2, 128, B, max_ctx, 2, partition_size=part)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(step.q)
-    say("work list order")
-    pkv.paged_attention_decode(out, step.q, step.k_cache, step.v_cache, step.tables, step.lens, cfg.scale, B, 2,
-                               max_ctx, partition_size=part, workspace=ws)
-    torch.cuda.synchronize()
+    shorter last partitions by non-increasing size, then empty sequences.
+    Returns the list."""
     raw = ws.cpu().numpy()
     n = int(raw[:4].view(np.int32)[0])
     pairs = raw[256:].view(np.int32)[: 2 * n].reshape(-1, 2)
@@ -220,7 +204,65 @@ def test_work_list_covers_every_partition_longest_first():
 
     rest = [size(x) for x in got[len(full):]]
     assert all(a >= b for a, b in zip(rest, rest[1:])), "last partitions must come longest first"
-    assert rest[-2:] == [0, 0], "empty sequences come last"
+    n_empty = int((lens == 0).sum())
+    assert rest[len(rest) - n_empty:] == [0] * n_empty, "empty sequences come last"
+    return got
+
+
+def test_work_list_covers_every_partition_longest_first():
+    rng = np.random.default_rng(17)
+    B, part = 16, 512
+    lens = rng.integers(1, 3000, size=37)
+    lens[[3, 20]] = 0
+    lens[7] = 512
+    lens[9] = 1024
+    cfg = _edge_cfg("bf16", 128, B, 4, 2).scaled(num_seqs=len(lens))
+    lay = make_layout(cfg, 21, lengths=lens)
+    step = DeviceStep.from_host(lay, host_values(lay))
+    max_ctx = int(lens.max())
+    need = pkv.workspace_bytes(len(lens), 4, 2, 128, B, max_ctx, 2, partition_size=part)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(step.q)
+    say("work list order")
+    pkv.paged_attention_decode(out, step.q, step.k_cache, step.v_cache, step.tables, step.lens, cfg.scale, B, 2,
+                               max_ctx, partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    _check_work_list(ws, lens, B, part)
+
+
+def test_work_list_of_a_batch_past_the_plans_register_cache():
+    """A batch of 700 sequences: the plan keeps the first 512 sequences'
+    lengths in registers between its passes and reads the rest again.  The
+    list must still name every partition once, in order, from both launches
+    that build it (the plain call's plan kernel and the decode step's first
+    launch), and every row must match the oracle."""
+    rng = np.random.default_rng(23)
+    B, part, S = 16, 64, 700
+    lens = rng.integers(1, 400, size=S)
+    lens[rng.choice(S, 9, replace=False)] = 0
+    lens[[5, 600, 699]] = [64, 128, 399]
+    cfg = _edge_cfg("bf16", 64, B, 2, 1).scaled(num_seqs=S)
+    lay = make_layout(cfg, 24, lengths=lens)
+    host = host_values(lay)
+    step = DeviceStep.from_host(lay, host)
+    max_ctx = int(lens.max())
+    need = pkv.workspace_bytes(S, 2, 1, 64, B, max_ctx, 2, partition_size=part)
+    say(f"work list past the register cache: S={S} partition={part}")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws_step = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out_step = torch.empty_like(step.q)
+    pkv.decode_step(out_step, step.q, step.k_new, step.v_new, step.k_cache, step.v_cache, step.slots, step.tables,
+                    step.lens, cfg.scale, B, 1, max_ctx, partition_size=part, workspace=ws_step)
+    out = torch.empty_like(step.q)
+    pkv.paged_attention_decode(out, step.q, step.k_cache, step.v_cache, step.tables, step.lens, cfg.scale, B, 1,
+                               max_ctx, partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    got = _check_work_list(ws, lens, B, part)
+    assert _check_work_list(ws_step, lens, B, part) == got, "the two launches built different lists"
+    assert torch.equal(out.view(torch.int16), out_step.view(torch.int16))
+    want, _, _ = oracle_step(lay, host)
+    err = assert_rows_close(widen(out), want, "bf16", "700 sequences")
+    record_error("work_list_700_sequences", err, partition=part)
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6, 8, 9, 10])
