@@ -310,25 +310,25 @@ int decode_arg_status(const void* out, const void* q, const void* k_cache, const
 
 namespace {
 
-// Decode attention; with `append`, the launch that builds the work list also
-// stores every sequence's new token (a decode step in two launches).
-int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* block_tables, const int32_t* context_lens, float scale,
-                int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
-                int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
-                int32_t num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append,
-                const int32_t* seq_start = nullptr, float* lse = nullptr) {
-  Plan plan;
+// The checks of a decode call on its workspace, then its kernel
+// parameters (no new tokens).  Touches no device memory.
+int decode_setup(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                 int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                 int32_t num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                 const pkv_attn_options* opts, const int32_t* seq_start, float* lse, Plan* plan,
+                 pkv::AttnParams* pp) {
   const int st = decode_checks(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                                block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
-                               max_blocks_per_seq, max_context_len, num_blocks, dtype, opts, &plan);
+                               max_blocks_per_seq, max_context_len, num_blocks, dtype, opts, plan);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
-  if (!workspace || workspace_bytes < plan.ws_bytes) return PKV_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < plan->ws_bytes) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 
-  pkv::AttnParams p;
+  pkv::AttnParams& p = *pp;
+  p = pkv::AttnParams{};
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;
@@ -337,29 +337,75 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.context_lens = context_lens;
   char* ws = static_cast<char*>(workspace);
   p.work = reinterpret_cast<pkv::WorkHeader*>(ws);
-  p.pairs = reinterpret_cast<pkv::WorkPair*>(ws + plan.pairs_off);
-  p.ws_o = plan.max_parts > 1 ? static_cast<void*>(ws + plan.ws_o_off) : nullptr;
-  p.ws_ml = plan.max_parts > 1 ? reinterpret_cast<float*>(ws + plan.ws_ml_off) : nullptr;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634 * (plan.fp8 ? (double)opts->k_scale : 1.0));
-  p.v_scale = plan.fp8 ? opts->v_scale : 1.f;
+  p.pairs = reinterpret_cast<pkv::WorkPair*>(ws + plan->pairs_off);
+  p.ws_o = plan->max_parts > 1 ? static_cast<void*>(ws + plan->ws_o_off) : nullptr;
+  p.ws_ml = plan->max_parts > 1 ? reinterpret_cast<float*>(ws + plan->ws_ml_off) : nullptr;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634 * (plan->fp8 ? (double)opts->k_scale : 1.0));
+  p.v_scale = plan->fp8 ? opts->v_scale : 1.f;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
   p.num_blocks = num_blocks;
-  p.part_blocks = plan.part_blocks;
-  p.max_parts = plan.max_parts;
-  p.max_pairs = (int32_t)plan.max_pairs;
-  p.window = plan.window;
+  p.part_blocks = plan->part_blocks;
+  p.max_parts = plan->max_parts;
+  p.max_pairs = (int32_t)plan->max_pairs;
+  p.window = plan->window;
   p.group = num_q_heads / num_kv_heads;
-  p.chunks = plan.chunks;
-  p.chunk_rows = plan.chunk_rows;
-  p.cap = plan.cap;
-  p.items = (int32_t)((int64_t)num_seqs * num_kv_heads * plan.max_parts);
+  p.chunks = plan->chunks;
+  p.chunk_rows = plan->chunk_rows;
+  p.cap = plan->cap;
+  p.items = (int32_t)((int64_t)num_seqs * num_kv_heads * plan->max_parts);
   p.seq_start = seq_start;
   p.lse = lse;
-  p.direct = plan.direct ? 1 : 0;
+  p.direct = plan->direct ? 1 : 0;
+  return PKV_OK;
+}
+
+// A call whose work list is in place (or not needed): the main kernel
+// between the optional timing events, then the split-K reduce.
+int decode_attend(const Plan& plan, const pkv::AttnParams& p, pkv_dtype dtype, int32_t head_dim,
+                  int32_t block_size, const pkv_attn_options* opts, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (opts && opts->main_begin_event) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  const bool have = plan.kernel == PKV_KERNEL_MFMA
+                        ? pkv::launch_attention_mfma(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
+                                                     head_dim, block_size, plan.cap, plan.keep, s, &err)
+                        : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
+                                                     head_dim, block_size, plan.cap, plan.keep, s, &err);
+  if (!have) return PKV_ERR_UNSUPPORTED;
+  if (err != hipSuccess) return launch_status(err);
+  if (opts && opts->main_end_event) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_end_event), s);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  if (plan.max_parts > 1) {
+    if (!pkv::launch_attention_reduce(p, dtype, head_dim, block_size, s, &err))
+      return PKV_ERR_UNSUPPORTED;
+    if (err != hipSuccess) return launch_status(err);
+  }
+  return PKV_OK;
+}
+
+// Decode attention; with `append`, the launch that builds the work list also
+// stores every sequence's new token (a decode step in two launches).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                int32_t num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                const pkv_attn_options* opts, void* stream, pkv::AppendArgs* append) {
+  Plan plan;
+  pkv::AttnParams p;
+  const int st = decode_setup(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                              num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                              max_context_len, num_blocks, dtype, workspace, workspace_bytes, opts,
+                              nullptr, nullptr, &plan, &p);
+  if (st != PKV_OK || num_seqs == 0) return st;
   // A small-grid decode step on the vector kernel (caches in the query
   // format) runs in one launch: the attention workgroups store the new
   // tokens and read them from the inputs.
@@ -383,27 +429,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     err = pkv::launch_attention_plan(p, block_size, s);
   }
   if (err != hipSuccess) return launch_status(err);
-  if (opts && opts->main_begin_event) {
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_begin_event), s);
-    if (e != hipSuccess) return launch_status(e);
-  }
-  const bool have = plan.kernel == PKV_KERNEL_MFMA
-                        ? pkv::launch_attention_mfma(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, plan.cap, plan.keep, s, &err)
-                        : pkv::launch_attention_valu(p, dtype, plan.fp8 ? PKV_FP8_E4M3 : dtype,
-                                                     head_dim, block_size, plan.cap, plan.keep, s, &err);
-  if (!have) return PKV_ERR_UNSUPPORTED;
-  if (err != hipSuccess) return launch_status(err);
-  if (opts && opts->main_end_event) {
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(opts->main_end_event), s);
-    if (e != hipSuccess) return launch_status(e);
-  }
-  if (plan.max_parts > 1) {
-    if (!pkv::launch_attention_reduce(p, dtype, head_dim, block_size, s, &err))
-      return PKV_ERR_UNSUPPORTED;
-    if (err != hipSuccess) return launch_status(err);
-  }
-  return PKV_OK;
+  return decode_attend(plan, p, dtype, head_dim, block_size, opts, s);
 }
 
 }  // namespace
@@ -567,38 +593,53 @@ int pkv_paged_attention_decode_shared_prefix(
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t vheads = num_q_heads * (num_groups > 0 ? group_size : 1);
-  if (num_groups > 0) {
-    pkv::PrefixArgs a;
-    a.q = static_cast<const char*>(q);
-    a.q_v = ws + L.q_v;
-    a.tables = block_tables;
-    a.tables_v = reinterpret_cast<int32_t*>(ws + L.tables_v);
-    a.prefix_lens = prefix_lens;
-    a.lens_v = reinterpret_cast<int32_t*>(ws + L.lens_v);
-    a.members = group_members;
-    a.num_seqs = num_seqs;
-    a.num_groups = num_groups;
-    a.group_size = group_size;
-    a.q_heads = num_q_heads;
-    a.group = num_q_heads / num_kv_heads;
-    a.row_pieces = head_dim * dtype_bytes(dtype) / 16;
-    a.max_blocks = max_blocks_per_seq;
-    a.tab_v = L.tab_v;
-    clear_pending_error();
-    const hipError_t e = pkv::launch_prefix_prep(a, s);
-    if (e != hipSuccess) return launch_status(e);
-    st = decode_impl(ws + L.o_v, ws + L.q_v, k_cache, v_cache, a.tables_v, a.lens_v, scale,
-                     block_size, num_kv_heads, num_groups, vheads, head_dim, L.tab_v,
-                     max_prefix_len, num_blocks, dtype, ws + L.ws_pre, L.ws_pre_bytes, &L.pre,
-                     stream, nullptr, nullptr, reinterpret_cast<float*>(ws + L.lse_v));
-    if (st != PKV_OK) return st;
+  if (num_groups == 0) {
+    return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                       max_context_len, num_blocks, dtype, ws + L.ws_suf, L.ws_suf_bytes, &L.suf,
+                       stream, nullptr);
   }
-  st = decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
-                   num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
-                   max_context_len, num_blocks, dtype, ws + L.ws_suf, L.ws_suf_bytes, &L.suf,
-                   stream, nullptr, num_groups > 0 ? prefix_lens : nullptr,
-                   reinterpret_cast<float*>(ws + L.lse_t));
-  if (st != PKV_OK || num_groups == 0) return st;
+  pkv::PrefixArgs a;
+  a.q = static_cast<const char*>(q);
+  a.q_v = ws + L.q_v;
+  a.tables = block_tables;
+  a.tables_v = reinterpret_cast<int32_t*>(ws + L.tables_v);
+  a.prefix_lens = prefix_lens;
+  a.lens_v = reinterpret_cast<int32_t*>(ws + L.lens_v);
+  a.members = group_members;
+  a.num_seqs = num_seqs;
+  a.num_groups = num_groups;
+  a.group_size = group_size;
+  a.q_heads = num_q_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.row_pieces = head_dim * dtype_bytes(dtype) / 16;
+  a.max_blocks = max_blocks_per_seq;
+  a.tab_v = L.tab_v;
+  // The two passes: the groups' shared prefixes (the virtual batch), then
+  // every sequence's own tokens from its prefix length on.
+  Plan pre_plan, suf_plan;
+  pkv::AttnParams pre, suf;
+  st = decode_setup(ws + L.o_v, ws + L.q_v, k_cache, v_cache, a.tables_v, a.lens_v, scale, block_size,
+                    num_kv_heads, num_groups, vheads, head_dim, L.tab_v, max_prefix_len, num_blocks,
+                    dtype, ws + L.ws_pre, L.ws_pre_bytes, &L.pre, nullptr,
+                    reinterpret_cast<float*>(ws + L.lse_v), &pre_plan, &pre);
+  if (st != PKV_OK) return st;
+  st = decode_setup(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                    num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                    max_context_len, num_blocks, dtype, ws + L.ws_suf, L.ws_suf_bytes, &L.suf,
+                    prefix_lens, reinterpret_cast<float*>(ws + L.lse_t), &suf_plan, &suf);
+  if (st != PKV_OK) return st;
+  // One launch builds the virtual batch and both work lists.
+  const bool reuse = opts && opts->reuse_plan;
+  a.plan_pre = !reuse && !pre_plan.direct;
+  a.plan_suf = !reuse && !suf_plan.direct;
+  clear_pending_error();
+  const hipError_t e = pkv::launch_prefix_prep(a, pre, suf, block_size, s);
+  if (e != hipSuccess) return launch_status(e);
+  st = decode_attend(pre_plan, pre, dtype, head_dim, block_size, &L.pre, s);
+  if (st != PKV_OK) return st;
+  st = decode_attend(suf_plan, suf, dtype, head_dim, block_size, &L.suf, s);
+  if (st != PKV_OK) return st;
   pkv::PrefixMergeArgs m;
   m.out = out;
   m.lse = reinterpret_cast<const float*>(ws + L.lse_t);

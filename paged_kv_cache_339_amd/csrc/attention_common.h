@@ -29,22 +29,26 @@ struct SeqWork {
   bool bad;     // context length outside what the table / launch covers
 };
 
-__device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
+// From the sequence's context length `raw` and, when the call has
+// per-sequence first tokens (p.seq_start), its first token `start`.
+__device__ __forceinline__ SeqWork seq_work_from(const AttnParams& p, int raw, int start, int B) {
   SeqWork w;
-  const int raw = p.context_lens[s];
   w.bad = raw < 0 || raw > p.max_context_len ||
           (int64_t)raw > (int64_t)p.max_blocks_per_seq * B;
   w.L = w.bad ? 0 : raw;
   w.t0 = (p.window > 0 && w.L > p.window) ? w.L - p.window : 0;
   if (p.seq_start != nullptr) {
-    const int st = p.seq_start[s];
-    if (st > w.t0) w.t0 = st;
+    if (start > w.t0) w.t0 = start;
     if (w.t0 >= w.L) w.L = w.t0 = 0;     // nothing left to attend to
   }
   w.blk0 = w.t0 / B;
   w.nblk = w.L > 0 ? (w.L + B - 1) / B - w.blk0 : 0;
   w.nparts = (w.nblk + p.part_blocks - 1) / p.part_blocks;
   return w;
+}
+
+__device__ __forceinline__ SeqWork seq_work(const AttnParams& p, int s, int B) {
+  return seq_work_from(p, p.context_lens[s], p.seq_start != nullptr ? p.seq_start[s] : 0, B);
 }
 
 // Safe reference point for 2^(x - m) when m may be -inf.

@@ -17,10 +17,11 @@
 // data) serve with one read of each prefix tile.
 //
 // Launches: prefix_prep_kernel (queries of each group's members side by
-// side, the group's table row and prefix length), the decode kernels on the
-// virtual batch, the decode kernels on the real batch starting each
-// sequence at its prefix length, and prefix_merge_kernel.
-#include "attention_common.h"
+// side, the group's table row and prefix length, and the work lists of both
+// passes), the decode kernels on the virtual batch, the decode kernels on the
+// real batch starting each sequence at its prefix length, and
+// prefix_merge_kernel.
+#include "attention_plan.h"
 
 namespace pkv {
 
@@ -34,17 +35,41 @@ __device__ __forceinline__ int first_member(const PrefixArgs& a, int vg) {
   return -1;
 }
 
-// Grid-stride over three index ranges: 16-byte pieces of the virtual query
-// rows, the virtual table entries, the virtual lengths.  Virtual head
+// The group's prefix length: its first valid member's (0 without one).
+__device__ __forceinline__ int group_prefix_len(const PrefixArgs& a, int vg) {
+  const int m = first_member(a, vg);
+  return m >= 0 ? a.prefix_lens[m] : 0;
+}
+
+// Workgroups 0 and 1 build the own-token and grouped passes' work lists (when
+// asked; the grouped pass's workgroup first writes the virtual lengths it
+// plans from, lane l the groups l + 64 k, the same groups it then reads).
+// The other workgroups grid-stride over three index ranges: 16-byte pieces
+// of the virtual query rows, the virtual table entries and (unless
+// workgroup 1 writes them) the virtual lengths.  Virtual head
 // vh = h Gs g + j g + i of group vg is query head h g + i of member j.
-__global__ __launch_bounds__(256) void prefix_prep_kernel(PrefixArgs a) {
+// Workgroups of one wave: the plan is one wave's work.
+__global__ __launch_bounds__(kWave) void prefix_prep_kernel(PrefixArgs a, AttnParams pre, AttnParams suf,
+                                                             int B) {
+  if (blockIdx.x == 0) {
+    if (a.plan_suf) plan_body(suf, B);
+    return;
+  }
+  if (blockIdx.x == 1) {
+    if (a.plan_pre) {
+      for (int vg = threadIdx.x; vg < a.num_groups; vg += kWave) a.lens_v[vg] = group_prefix_len(a, vg);
+      __syncthreads();
+      plan_body(pre, B);
+    }
+    return;
+  }
   const int64_t vrows = (int64_t)a.num_groups * a.q_heads * a.group_size;
   const int64_t n_q = vrows * a.row_pieces;
   const int64_t n_t = (int64_t)a.num_groups * a.tab_v;
-  const int64_t n = n_q + n_t + a.num_groups;
+  const int64_t n = n_q + n_t + (a.plan_pre ? 0 : a.num_groups);
   const int per_kv = a.group_size * a.group;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = (blockIdx.x - 2) * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)(gridDim.x - 2) * blockDim.x) {
     if (i < n_q) {
       const int64_t row = i / a.row_pieces;
       const int piece = (int)(i - row * a.row_pieces);
@@ -63,8 +88,7 @@ __global__ __launch_bounds__(256) void prefix_prep_kernel(PrefixArgs a) {
       a.tables_v[k] = m >= 0 ? a.tables[(size_t)m * a.max_blocks + b] : -1;
     } else {
       const int vg = (int)(i - n_q - n_t);
-      const int m = first_member(a, vg);
-      a.lens_v[vg] = m >= 0 ? a.prefix_lens[m] : 0;
+      a.lens_v[vg] = group_prefix_len(a, vg);
     }
   }
 }
@@ -105,12 +129,12 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefixMergeArgs a) {
   store_row8<DT, false>(a.out, orow * D + d, r);
 }
 
-hipError_t launch_prefix_prep(const PrefixArgs& a, hipStream_t st) {
+hipError_t launch_prefix_prep(const PrefixArgs& a, const AttnParams& pre, const AttnParams& suf,
+                              int block_size, hipStream_t st) {
   const int64_t n = (int64_t)a.num_groups * a.q_heads * a.group_size * a.row_pieces +
                     (int64_t)a.num_groups * a.tab_v + a.num_groups;
-  if (n == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-  hipLaunchKernelGGL(prefix_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  const int64_t blocks = 2 + std::min<int64_t>((n + kWave - 1) / kWave, 32768);
+  hipLaunchKernelGGL(prefix_prep_kernel, dim3((unsigned)blocks), dim3(kWave), 0, st, a, pre, suf, block_size);
   return hipGetLastError();
 }
 

@@ -148,6 +148,9 @@ struct PrefixArgs {
   int32_t* lens_v;            // [Gn] (workspace)
   const int32_t* members;     // [Gn, Gs], -1 = unused slot
   int32_t num_seqs, num_groups, group_size, q_heads, group, row_pieces, max_blocks, tab_v;
+  // Work lists the same launch builds: the grouped pass's (which then also
+  // writes lens_v, from which it plans) and the own-token pass's.
+  int32_t plan_pre, plan_suf;
 };
 
 struct PrefixMergeArgs {
@@ -159,7 +162,11 @@ struct PrefixMergeArgs {
   int32_t num_seqs, num_groups, group_size, q_heads, group;
 };
 
-hipError_t launch_prefix_prep(const PrefixArgs& a, hipStream_t stream);
+// The shared-prefix call's first launch: the virtual batch (queries side by
+// side, tables, lengths) and the two passes' work lists.  `pre` / `suf`: the
+// grouped and own-token passes' parameters (used when a.plan_pre / a.plan_suf).
+hipError_t launch_prefix_prep(const PrefixArgs& a, const AttnParams& pre, const AttnParams& suf,
+                              int block_size, hipStream_t stream);
 bool launch_prefix_merge(const PrefixMergeArgs& a, pkv_dtype dt, int head_dim, hipStream_t stream,
                          hipError_t* err);
 
